@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the row-exact few-row mat-vec.
+
+This module only draws random bytes and writes them into block fields.  It
+decodes nothing and computes no product: both the oracle and the HIP path
+take its output as input, and neither is imported here.
+
+Random numbers come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014), vectorised over a counter:
+output ``i`` of stream ``seed`` is ``mix(seed + (i + 1) * 0x9E3779B97F4A7C15)``.
+Normals use the Box-Muller transform in float64.  Half-precision fields are
+rounded to nearest-even by numpy's float64 -> float16 conversion.
+
+Block field offsets follow the GGML block structs named by the weight types
+(Q8_0, Q4_K, Q6_K, Q5_0); the byte sizes are those of the mlx-native
+``row_exact_matvec`` page (block constants).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+F16, Q8_0, Q4_K, Q6_K, Q5_0 = 0, 1, 2, 3, 4
+TYPE_NAMES = {F16: "F16", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_0: "Q5_0"}
+NAME_TYPES = {v: k for k, v in TYPE_NAMES.items()}
+
+# (values per block, bytes per block)
+BLOCK = {F16: (1, 2), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q5_0: (32, 22)}
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+
+def splitmix64(seed: int, count: int, offset: int = 0) -> np.ndarray:
+    """``count`` outputs of SplitMix64 stream ``seed`` starting at output ``offset``."""
+    with np.errstate(over="ignore"):
+        i = np.arange(offset + 1, offset + count + 1, dtype=np.uint64)
+        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + i * _GOLDEN
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        return z ^ (z >> np.uint64(31))
+
+
+class Stream:
+    """Sequential draws from one SplitMix64 stream."""
+
+    def __init__(self, seed: int):
+        self.seed = seed
+        self.pos = 0
+
+    def u64(self, count: int) -> np.ndarray:
+        out = splitmix64(self.seed, count, self.pos)
+        self.pos += count
+        return out
+
+    def bytes(self, count: int) -> np.ndarray:
+        words = self.u64((count + 7) // 8)
+        return words.view(np.uint8)[:count].copy()
+
+    def uniform(self, count: int) -> np.ndarray:
+        """Doubles in [0, 1) from the top 53 bits."""
+        return (self.u64(count) >> np.uint64(11)).astype(np.float64) * (1.0 / (1 << 53))
+
+    def normal(self, count: int) -> np.ndarray:
+        """Standard normals, Box-Muller in float64 (one normal per pair)."""
+        u1 = self.uniform(count)
+        u2 = self.uniform(count)
+        return np.sqrt(-2.0 * np.log1p(-u1)) * np.cos(2.0 * np.pi * u2)
+
+    def ints(self, count: int, lo: int, hi: int) -> np.ndarray:
+        """Integers uniform on [lo, hi] (inclusive), via floor(u * span)."""
+        span = hi - lo + 1
+        return (np.floor(self.uniform(count) * span).astype(np.int64) + lo)
+
+
+def _f16_bits(values: np.ndarray) -> np.ndarray:
+    return values.astype(np.float16).view(np.uint16)
+
+
+def _put_u16(blocks: np.ndarray, offset: int, bits: np.ndarray) -> None:
+    blocks[:, offset] = (bits & 0xFF).astype(np.uint8)
+    blocks[:, offset + 1] = (bits >> 8).astype(np.uint8)
+
+
+def weights(wtype: int, rows: int, k: int, seed: int) -> np.ndarray:
+    """Row-major weight bytes, ``rows`` rows of ``k`` values, drawn as in the
+    synthetic workload recipe:
+
+    - F16: N(0, 0.02) rounded to half.
+    - Q8_0: d = half(|N(0,1)| * 0.01); 32 int8 uniform on [-127, 127].
+    - Q4_K: d, dmin = half(|N(0,1)| * 0.01); 12 scale bytes and 128 quant bytes
+      uniform (all 6-bit scales/mins and 4-bit quants uniform).
+    - Q6_K: 128 low-bit and 64 high-bit bytes uniform; 16 int8 scales uniform
+      on [-64, 63]; d = half(|N(0,1)| * 0.001).
+    - Q5_0: d = half(|N(0,1)| * 0.01); 4 high-bit and 16 nibble bytes uniform.
+    """
+    per, nbytes = BLOCK[wtype]
+    if k % (4 if wtype == F16 else per):
+        raise ValueError(f"k={k} is not a multiple of the block size of {TYPE_NAMES[wtype]}")
+    s = Stream(seed)
+    if wtype == F16:
+        vals = s.normal(rows * k) * 0.02
+        return _f16_bits(vals).view(np.uint8).reshape(rows, 2 * k).copy()
+    nblk = rows * (k // per)
+    blocks = s.bytes(nblk * nbytes).reshape(nblk, nbytes)
+    if wtype == Q8_0:
+        _put_u16(blocks, 0, _f16_bits(np.abs(s.normal(nblk)) * 0.01))
+        blocks[:, 2:34] = s.ints(nblk * 32, -127, 127).astype(np.int8).view(np.uint8).reshape(nblk, 32)
+    elif wtype == Q4_K:
+        _put_u16(blocks, 0, _f16_bits(np.abs(s.normal(nblk)) * 0.01))
+        _put_u16(blocks, 2, _f16_bits(np.abs(s.normal(nblk)) * 0.01))
+    elif wtype == Q6_K:
+        blocks[:, 192:208] = s.ints(nblk * 16, -64, 63).astype(np.int8).view(np.uint8).reshape(nblk, 16)
+        _put_u16(blocks, 208, _f16_bits(np.abs(s.normal(nblk)) * 0.001))
+    elif wtype == Q5_0:
+        _put_u16(blocks, 0, _f16_bits(np.abs(s.normal(nblk)) * 0.01))
+    else:
+        raise ValueError(f"unknown weight type {wtype}")
+    return blocks.reshape(rows, (k // per) * nbytes)
+
+
+def activations(rows: int, cols: int, seed: int) -> np.ndarray:
+    """``rows x cols`` float32 ~ N(0, 1)."""
+    return Stream(seed).normal(rows * cols).astype(np.float32).reshape(rows, cols)
+
+
+def row_bytes(wtype: int, k: int) -> int:
+    per, nbytes = BLOCK[wtype]
+    return (k // per) * nbytes
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: weight type, shape, strides and the m set."""
+
+    name: str
+    wtype: int
+    n: int
+    k: int
+    batch: int
+    ms: Tuple[int, ...]
+    index: int
+    grouped: bool = False
+
+    @property
+    def w_seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def x_seed(self) -> int:
+        return 2000 + self.index
+
+    def strides(self, m: int) -> Tuple[int, int, int, int]:
+        """(x_row, x_batch, y_row, y_batch) in elements."""
+        if self.grouped:
+            return (self.batch * self.k, self.k, self.batch * self.n, self.n)
+        return (self.k, 0, self.n, 0)
+
+    @property
+    def weight_bytes(self) -> int:
+        return row_bytes(self.wtype, self.k) * self.n * self.batch
+
+    def make_weights(self) -> np.ndarray:
+        return weights(self.wtype, self.n * self.batch, self.k, self.w_seed)
+
+    def make_x(self, m: int = 8) -> np.ndarray:
+        """x for ``m`` rows (drawn as 8 rows; an m-row run uses rows 0..m-1).
+
+        Contiguous layout: shape ``[m, k]``.  Grouped token-major layout:
+        shape ``[m, batch * k]``.
+        """
+        cols = self.batch * self.k if self.grouped else self.k
+        return activations(8, cols, self.x_seed)[:m].copy()
+
+
+# The five workload configurations of the row-exact mat-vec (index = seed offset).
+WORKLOADS: List[Workload] = [
+    Workload("f16_256x512", F16, 256, 512, 1, tuple(range(1, 9)), 0),
+    Workload("q8_0_4096x4096", Q8_0, 4096, 4096, 1, (1, 4, 8), 1),
+    Workload("q4_k_14336x4096", Q4_K, 14336, 4096, 1, tuple(range(1, 9)), 2),
+    Workload("q6_k_4096x14336", Q6_K, 4096, 14336, 1, (1, 8), 3),
+    Workload("q6_k_128256x4096", Q6_K, 128256, 4096, 1, (1, 8), 4),
+    Workload("q5_0_16x1024x4096_grouped", Q5_0, 1024, 4096, 16, (8,), 5, grouped=True),
+]
+BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
+
+
+def get(name: str) -> Workload:
+    return BY_NAME[name]
+
+
+def scaled(w: Workload, n: Optional[int] = None, k: Optional[int] = None,
+           batch: Optional[int] = None) -> Workload:
+    """Same recipe and seeds at a different size (for oracle-sized tests)."""
+    return dataclasses.replace(w, name=w.name + "_scaled", n=n or w.n, k=k or w.k,
+                               batch=batch or w.batch)
