@@ -1,0 +1,181 @@
+/*
+ * row_exact_mv.h — C ABI of the row-exact few-row mat-vec for MI355X (gfx950).
+ *
+ *   y[b][j][i] = sum_kk W[b*n + i][kk] * x[b][j][kk]
+ *
+ * for 1 <= m <= 8 float32 input rows j, n weight rows i per batch, k inner
+ * values, batch independent products; F16, Q8_0, Q4_K, Q6_K or Q5_0 weights,
+ * float32 output.  Defined by mlx-native 0.18.0, src/ops/row_exact_matvec.rs:
+ * module docs (the product, "Row exactness", "Batched / grouped products"),
+ * RowExactWeight, RowExactMatvecShape, RowExactMatvecSchedule, validate(),
+ * dispatch_row_exact_matvec and dispatch_row_exact_matvec_scheduled.
+ *
+ * Row exactness: output row j is bitwise identical whether it is computed with
+ * m = 1 or as one row of any m <= 8, and identical across repeated calls.  The
+ * only thing that changes the bits of an output is the reduction split
+ * (row_exact_schedule_t.k_split), which the library derives from the weight
+ * type and k alone; every other schedule field only packs work.
+ *
+ * Conventions for every entry point:
+ *  - Pointers W, x, y, out are device pointers (HBM).  The caller owns them;
+ *    the library keeps no reference after the call returns.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; 0 = the null stream)
+ *    and never synchronize.  Results are defined once the stream reaches the
+ *    enqueued kernels.  Inputs must not change until then.
+ *  - Return 0 on success or a negative ROW_EXACT_E* code.  Every argument is
+ *    checked before anything is enqueued: on error nothing is launched and y
+ *    is untouched.  row_exact_last_error() then describes the failure.
+ *  - Thread safety: calls may come from several host threads; the error text
+ *    is per thread.
+ */
+#ifndef ROW_EXACT_MV_H
+#define ROW_EXACT_MV_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight storage (RowExactWeight; same order as its index()).
+ *  F16  : row-major [batch*n, k] IEEE half; k % 4 == 0; W 8-byte aligned.
+ *  Q8_0 : row-major [batch*n, k/32] blocks of 34 bytes (f16 d, 32 int8);
+ *         k % 32 == 0; W 4-byte aligned.
+ *  Q4_K : row-major [batch*n, k/256] super-blocks of 144 bytes (f16 d, f16
+ *         dmin, 12 bytes of 6-bit scales/mins, 128 bytes of nibbles);
+ *         k % 256 == 0; W 16-byte aligned.
+ *  Q6_K : row-major [batch*n, k/256] super-blocks of 210 bytes (128 bytes of
+ *         low nibbles, 64 bytes of 2-bit highs, 16 int8 scales, f16 d);
+ *         k % 256 == 0; W 4-byte aligned.
+ *  Q5_0 : row-major [batch*n, k/32] blocks of 22 bytes (f16 d, 32 high bits,
+ *         16 bytes of nibbles); k % 32 == 0; W 4-byte aligned.
+ * Block layouts are those of the GGML types of the same names (the pages give
+ * their byte sizes only).  The page's dispatcher accepts 2-byte-aligned
+ * Q8_0 / Q6_K / Q5_0 weights; this library reads them with dword loads and
+ * asks for 4-byte alignment of W (rows inside may sit at any even offset). */
+typedef enum {
+    ROW_EXACT_F16 = 0,
+    ROW_EXACT_Q8_0 = 1,
+    ROW_EXACT_Q4_K = 2,
+    ROW_EXACT_Q6_K = 3,
+    ROW_EXACT_Q5_0 = 4
+} row_exact_weight_t;
+
+/* Maximum input rows per call (ROW_EXACT_MATVEC_MAX_ROWS). */
+#define ROW_EXACT_MAX_ROWS 8
+
+/* Element strides of x and y (RowExactMatvecShape).  x row/batch strides must
+ * be multiples of 4; the x pointer 16-byte aligned; the y pointer 4-byte
+ * aligned.  Passing NULL selects the contiguous layout x [m, k], y [m, n],
+ * batch strides 0 (RowExactMatvecShape::contiguous).  The grouped token-major
+ * layout of RowExactMatvecShape::grouped_token_major is
+ * {groups*k, k, groups*n, n} with batch = groups. */
+typedef struct {
+    uint32_t x_row_stride;
+    uint32_t x_batch_stride;
+    uint32_t y_row_stride;
+    uint32_t y_batch_stride;
+} row_exact_strides_t;
+
+/* Launch schedule (RowExactMatvecSchedule, re-planned for CDNA4 wave64).
+ *  k_split              : numerics.  Waves whose partial sums form one output
+ *                         (1: the 64 lanes of one wave split K and a fixed
+ *                         DPP/permlane tree reduces them).  Derived from
+ *                         (weight type, k) by row_exact_schedule(); a pinned
+ *                         schedule must carry the same value.
+ *  rows_per_wave        : packing.  Weight rows a wave streams together,
+ *                         sharing each input load: 1, 2 or 4.
+ *  waves_per_workgroup  : packing.  1..8 (64..512 threads).
+ *  workgroups_per_batch : packing.  Grid x; batch is grid y (batch-major).
+ *  k_chunk              : packing.  Input values per row staged in LDS per
+ *                         pass; >= k means one pass.  Otherwise a multiple of
+ *                         the weight type's wave step (512 values for F16,
+ *                         2048 for Q8_0 / Q4_K / Q5_0, 4096 for Q6_K).
+ * Packing fields never change the bits of y. */
+typedef struct {
+    uint32_t k_split;
+    uint32_t rows_per_wave;
+    uint32_t waves_per_workgroup;
+    uint32_t workgroups_per_batch;
+    uint32_t k_chunk;
+} row_exact_schedule_t;
+
+/* Error codes. */
+#define ROW_EXACT_OK 0
+#define ROW_EXACT_EARG (-1)      /* weight type, m, n, k, batch, k multiple, NULL pointer */
+#define ROW_EXACT_EALIGN (-2)    /* W / x / y pointer alignment */
+#define ROW_EXACT_ESTRIDE (-3)   /* x strides not multiples of 4 */
+#define ROW_EXACT_EALIAS (-4)    /* output views overlap each other, W or x */
+#define ROW_EXACT_EEXTENT (-5)   /* sizes overflow 64-bit byte offsets */
+#define ROW_EXACT_ESCHEDULE (-6) /* pinned schedule invalid, or over the device's limits */
+#define ROW_EXACT_EHIP (-7)      /* HIP runtime error (device query or launch) */
+
+/* Enqueue y[b, j, :] = W[b] . x[b, j, :] for b < batch, j < m with the
+ * default schedule (dispatch_row_exact_matvec).
+ *  wt      : weight storage, see row_exact_weight_t.
+ *  W       : device pointer to batch*n rows of row_exact_row_bytes(wt, k)
+ *            bytes; batch b starts at b * n * row_bytes.
+ *  x       : device float32, element (b, j, kk) at b*x_batch_stride +
+ *            j*x_row_stride + kk.
+ *  y       : device float32, element (b, j, i) at b*y_batch_stride +
+ *            j*y_row_stride + i.  Only these m*n*batch elements are written.
+ *  n, k, m, batch : n, k, batch >= 1; 1 <= m <= 8.
+ *  strides : NULL for contiguous; see row_exact_strides_t.
+ *  stream  : HIP stream to enqueue on.
+ * Errors: ROW_EXACT_EARG, EALIGN, ESTRIDE, EALIAS (output rows/batches must
+ * write disjoint elements, the four layout cases of validate(); y's byte range
+ * must not overlap W's or x's), EEXTENT, EHIP. */
+int row_exact_mv(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n, uint32_t k,
+                 uint32_t m, uint32_t batch, const row_exact_strides_t *strides, hipStream_t stream);
+
+/* As row_exact_mv with an explicit schedule
+ * (dispatch_row_exact_matvec_scheduled).  Outputs are bitwise identical to
+ * row_exact_mv's for every valid schedule: packing is inert and k_split must
+ * equal the derived value.  Extra error: ROW_EXACT_ESCHEDULE (a field out of
+ * range, k_chunk not a wave-step multiple, LDS need above the device limit). */
+int row_exact_mv_scheduled(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n,
+                           uint32_t k, uint32_t m, uint32_t batch, const row_exact_strides_t *strides,
+                           const row_exact_schedule_t *schedule, hipStream_t stream);
+
+/* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
+ * depends on (wt, k) only; the packing fields may depend on every argument
+ * and on the current device.  Writes *out; errors: EARG, EHIP. */
+int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                       row_exact_schedule_t *out);
+
+/* Bytes per weight row of k values (RowExactWeight::row_bytes):
+ * F16 2k; Q8_0 34*(k/32); Q4_K 144*(k/256); Q6_K 210*(k/256); Q5_0 22*(k/32).
+ * Returns 0 for an unknown type. */
+uint64_t row_exact_row_bytes(row_exact_weight_t wt, uint32_t k);
+
+/* Bytes the product reads or writes (validate()'s size checks; strided_extent
+ * = last element + 1): *w_bytes = row_bytes * n * batch;
+ * *x_bytes = 4 * ((batch-1)*x_batch_stride + (m-1)*x_row_stride + k);
+ * *y_bytes = 4 * ((batch-1)*y_batch_stride + (m-1)*y_row_stride + n).
+ * strides NULL = contiguous.  Any output pointer may be NULL.
+ * Errors: EARG, EEXTENT. */
+int row_exact_required_bytes(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                             const row_exact_strides_t *strides, uint64_t *w_bytes, uint64_t *x_bytes,
+                             uint64_t *y_bytes);
+
+/* Enqueue out[r*k + v] = float32 value of weight v of row r, for rows
+ * consecutive weight rows at W.  Uses the same device block decoders as the
+ * mat-vec.  out must be 4-byte aligned and not overlap W.
+ * Errors: EARG, EALIGN, EALIAS, EEXTENT, EHIP. */
+int row_exact_dequant(row_exact_weight_t wt, const void *W, float *out, uint32_t rows, uint32_t k,
+                      hipStream_t stream);
+
+/* Text of the calling thread's last error ("" if none); prefixed
+ * "row_exact_mv: ".  Valid until the thread's next call. */
+const char *row_exact_last_error(void);
+
+/* Number of kernels this process has enqueued through the library. */
+uint64_t row_exact_launch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROW_EXACT_MV_H */

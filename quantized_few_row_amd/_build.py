@@ -1,0 +1,68 @@
+"""Build ``librow_exact_mv.so`` in-tree with hipcc for gfx950.
+
+Every HIP translation unit is compiled with packed-FP32 instruction
+selection disabled and floating-point contraction off (all FMAs in the
+kernels are explicit), then linked into one shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "librow_exact_mv.so")
+ARCH = os.environ.get("ROW_EXACT_ARCH", "gfx950")
+
+SOURCES = ["re_api.hip", "re_mv_f16.hip", "re_mv_q8_0.hip", "re_mv_q4_k.hip", "re_mv_q6_k.hip", "re_mv_q5_0.hip"]
+HEADERS = ["re_internal.h", "re_kernels.h"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def compile_flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-ffp-contract=off", "-fno-fast-math", "-I", INCLUDE, "-I", CSRC]
+
+
+def build(jobs: int = 6, verbose: bool = False) -> str:
+    """Compile every HIP source (always) and link the shared library."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    flags = compile_flags()
+
+    def one(src: str) -> str:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        cmd = [cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr[-4000:]}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr[-4000:]}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

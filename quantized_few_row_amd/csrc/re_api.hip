@@ -1,0 +1,431 @@
+// Host side of the row-exact mat-vec C ABI: argument checks, schedule and
+// launch.  The checks restate mlx-native 0.18.0 src/ops/row_exact_matvec.rs
+// validate() (shape, schedule, k multiple, strides and offsets, output
+// aliasing, sizes); the schedule is this library's own (wave64 pieces,
+// rows per wave, LDS passes).
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "re_internal.h"
+#include "row_exact_mv.h"
+
+using namespace rex;
+
+namespace {
+
+thread_local std::string g_err;
+std::atomic<uint64_t> g_launches{0};
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = std::string("row_exact_mv: ") + buf;
+    return code;
+}
+
+const char *type_name(int t) {
+    static const char *names[] = {"F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0"};
+    return (t >= 0 && t <= 4) ? names[t] : "?";
+}
+
+bool valid_type(int t) { return t >= 0 && t <= 4; }
+
+uint32_t k_multiple(int t) {
+    switch (t) {
+    case kF16: return 4;
+    case kQ8_0: case kQ5_0: return 32;
+    default: return 256;
+    }
+}
+
+// Weight pointer alignment this library needs (the page asks 8 / 2 / 16 / 2 / 2).
+uint32_t w_align(int t) {
+    switch (t) {
+    case kF16: return 8;
+    case kQ4K: return 16;
+    default: return 4;
+    }
+}
+
+uint64_t row_bytes_of(int t, uint32_t k) {
+    switch (t) {
+    case kF16: return (uint64_t)k * 2;
+    case kQ8_0: return (uint64_t)(k / 32) * 34;
+    case kQ4K: return (uint64_t)(k / 256) * 144;
+    case kQ6K: return (uint64_t)(k / 256) * 210;
+    case kQ5_0: return (uint64_t)(k / 32) * 22;
+    default: return 0;
+    }
+}
+
+struct DevInfo {
+    int cus = 0;
+    size_t lds_max = 0;
+    bool ok = false;
+};
+
+int device_info(DevInfo &out) {
+    static std::mutex mu;
+    static DevInfo cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 64 && cache[dev].ok) {
+        out = cache[dev];
+        return 0;
+    }
+    int cus = 0, lds = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "device query: %s", hipGetErrorString(e));
+    DevInfo d;
+    d.cus = cus > 0 ? cus : 1;
+    d.lds_max = (size_t)(lds > 0 ? lds : 65536);
+    d.ok = true;
+    if (dev >= 0 && dev < 64) cache[dev] = d;
+    out = d;
+    return 0;
+}
+
+// Floats per staged x row for kc values (4 pad floats per pad period).
+uint32_t xs_stride(int t, uint32_t kc) {
+    const uint32_t padp = pad_period(t);
+    return kc + 4 * ((kc + padp - 1) / padp);
+}
+
+size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
+    const uint32_t kc = k_chunk < k ? k_chunk : k;
+    return (size_t)m * xs_stride(t, kc) * sizeof(float);
+}
+
+typedef unsigned __int128 u128;
+
+// (batch-1)*bs + (rows-1)*rs + cols, the last element + 1 of a strided view.
+u128 extent(uint32_t batch, uint64_t bs, uint32_t rows, uint64_t rs, uint64_t cols) {
+    return (u128)(batch - 1) * bs + (u128)(rows - 1) * rs + cols;
+}
+
+row_exact_strides_t resolve_strides(const row_exact_strides_t *s, uint32_t m, uint32_t n, uint32_t k) {
+    if (s) return *s;
+    row_exact_strides_t c;
+    c.x_row_stride = k;
+    c.x_batch_stride = 0;
+    c.y_row_stride = n;
+    c.y_batch_stride = 0;
+    (void)m;
+    return c;
+}
+
+// Shape checks shared by every entry point (validate(): m, n/k/batch, k multiple).
+int check_shape(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch) {
+    if (!valid_type(t)) return fail(ROW_EXACT_EARG, "unknown weight type %d", t);
+    if (m == 0 || m > ROW_EXACT_MAX_ROWS) return fail(ROW_EXACT_EARG, "m (%u) must be in 1..=8", m);
+    if (n == 0 || k == 0 || batch == 0)
+        return fail(ROW_EXACT_EARG, "n (%u), k (%u) and batch (%u) must be > 0", n, k, batch);
+    if (k % k_multiple(t))
+        return fail(ROW_EXACT_EARG, "k (%u) must be a multiple of %u for %s", k, k_multiple(t), type_name(t));
+    return 0;
+}
+
+int sizes(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, const row_exact_strides_t &s, uint64_t &wb,
+          uint64_t &xb, uint64_t &yb) {
+    const u128 w = (u128)row_bytes_of(t, k) * n * batch;
+    const u128 x = extent(batch, s.x_batch_stride, m, s.x_row_stride, k) * 4;
+    const u128 y = extent(batch, s.y_batch_stride, m, s.y_row_stride, n) * 4;
+    const u128 lim = (u128)1 << 62;
+    if (w >= lim || x >= lim || y >= lim)
+        return fail(ROW_EXACT_EEXTENT, "operand sizes overflow 64-bit byte offsets");
+    wb = (uint64_t)w;
+    xb = (uint64_t)x;
+    yb = (uint64_t)y;
+    return 0;
+}
+
+bool overlap(uintptr_t a, uint64_t an, uintptr_t b, uint64_t bn) { return a < b + bn && b < a + an; }
+
+int validate_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                const row_exact_strides_t &s, uint64_t &wb, uint64_t &xbytes, uint64_t &ybytes) {
+    int rc = check_shape(t, n, k, m, batch);
+    if (rc) return rc;
+    if (!W || !x || !y) return fail(ROW_EXACT_EARG, "W, x and y must be non-NULL device pointers");
+    if (s.x_row_stride % 4 || s.x_batch_stride % 4 || ((uintptr_t)x % 16))
+        return fail(s.x_row_stride % 4 || s.x_batch_stride % 4 ? ROW_EXACT_ESTRIDE : ROW_EXACT_EALIGN,
+                    "input strides (%u, %u) must be multiples of 4 and the input pointer 16-byte aligned "
+                    "(offset %u)",
+                    s.x_row_stride, s.x_batch_stride, (unsigned)((uintptr_t)x % 16));
+    if ((uintptr_t)W % w_align(t) || (uintptr_t)y % 4)
+        return fail(ROW_EXACT_EALIGN, "weight pointer (offset %u) must be %u-byte and output (offset %u) 4-byte aligned",
+                    (unsigned)((uintptr_t)W % 16), w_align(t), (unsigned)((uintptr_t)y % 4));
+    // Output elements must not alias (either layout order is accepted).
+    const uint64_t yrs = s.y_row_stride, ybs = s.y_batch_stride;
+    const bool rows_disjoint = m == 1 || yrs >= n;
+    bool ok;
+    if (batch == 1)
+        ok = rows_disjoint;
+    else if (m == 1)
+        ok = ybs >= n;
+    else if (yrs >= ybs)
+        ok = ybs >= n && (u128)yrs >= (u128)(batch - 1) * ybs + n;
+    else
+        ok = rows_disjoint && (u128)ybs >= (u128)(m - 1) * yrs + n;
+    if (!ok)
+        return fail(ROW_EXACT_EALIAS, "output strides overlap: y_row_stride %u, y_batch_stride %u, m %u, n %u, batch %u",
+                    s.y_row_stride, s.y_batch_stride, m, n, batch);
+    rc = sizes(t, n, k, m, batch, s, wb, xbytes, ybytes);
+    if (rc) return rc;
+    if (row_bytes_of(t, k) > 0x7fffffffull)
+        return fail(ROW_EXACT_EEXTENT, "a weight row of %llu bytes exceeds 2^31 - 1",
+                    (unsigned long long)row_bytes_of(t, k));
+    if (overlap((uintptr_t)y, ybytes, (uintptr_t)W, wb) || overlap((uintptr_t)y, ybytes, (uintptr_t)x, xbytes))
+        return fail(ROW_EXACT_EALIAS, "output range overlaps the weight or input range");
+    return 0;
+}
+
+// Reduction split: a function of (type, k) only.  Every output is the
+// 64-lane tree sum of one wave's lane chains.
+uint32_t derived_k_split(int, uint32_t) { return 1; }
+
+int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, row_exact_schedule_t &s) {
+    DevInfo di;
+    int rc = device_info(di);
+    if (rc) return rc;
+    s.k_split = derived_k_split(t, k);
+    // rows per wave: the most that still leaves >= 8 waves per CU
+    const uint64_t rows = (uint64_t)n * batch;
+    const uint64_t target_waves = (uint64_t)di.cus * 8;
+    uint32_t nr = 4;
+    while (nr > 1 && rows / nr < target_waves) nr >>= 1;
+    s.rows_per_wave = nr;
+    const uint32_t gpb = (n + nr - 1) / nr;
+    uint32_t waves = 8;
+    while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
+    s.waves_per_workgroup = waves;
+    // LDS passes: one if the m staged rows fit, else the largest wave-step multiple that fits
+    const uint32_t step = wave_step_values(t);
+    uint32_t kc = k;
+    if (lds_bytes(t, m, k, k) > di.lds_max) {
+        kc = step;
+        while (kc + step < k && lds_bytes(t, m, k, kc + step) <= di.lds_max) kc += step;
+    }
+    s.k_chunk = kc;
+    // workgroups: single pass -> persistent-ish, up to 2 per CU; several passes -> one row group per wave
+    const uint32_t max_wgs = (gpb + waves - 1) / waves;
+    uint32_t wgs;
+    if (kc >= k) {
+        const size_t l = lds_bytes(t, m, k, kc);
+        uint64_t per_cu = l ? di.lds_max / l : 2;
+        if (per_cu < 1) per_cu = 1;
+        if (per_cu > 2) per_cu = 2;
+        const uint64_t target = (uint64_t)di.cus * per_cu;
+        uint64_t w = (target + batch - 1) / batch;
+        if (w < 1) w = 1;
+        wgs = (uint32_t)(w < max_wgs ? w : max_wgs);
+    } else {
+        wgs = max_wgs;
+    }
+    s.workgroups_per_batch = wgs;
+    return 0;
+}
+
+// Checks that need no device (every field's range).
+int check_schedule_fields(int t, uint32_t k, const row_exact_schedule_t &s) {
+    const uint32_t ks = derived_k_split(t, k);
+    if (s.k_split != ks)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule k_split (%u) must be %u for %s with k = %u", s.k_split, ks,
+                    type_name(t), k);
+    if (!(s.rows_per_wave == 1 || s.rows_per_wave == 2 || s.rows_per_wave == 4))
+        return fail(ROW_EXACT_ESCHEDULE, "schedule rows_per_wave (%u) must be 1, 2 or 4", s.rows_per_wave);
+    if (s.waves_per_workgroup < 1 || s.waves_per_workgroup > 8)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be in 1..=8", s.waves_per_workgroup);
+    if (s.workgroups_per_batch < 1)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule workgroups_per_batch must be >= 1");
+    const uint32_t step = wave_step_values(t);
+    if (s.k_chunk < k && (s.k_chunk == 0 || s.k_chunk % step))
+        return fail(ROW_EXACT_ESCHEDULE, "schedule k_chunk (%u) must be >= k (%u) or a multiple of %u for %s",
+                    s.k_chunk, k, step, type_name(t));
+    return 0;
+}
+
+// Checks against the current device's limits.
+int check_schedule_device(int t, uint32_t k, uint32_t m, const row_exact_schedule_t &s, const DevInfo &di) {
+    const size_t l = lds_bytes(t, m, k, s.k_chunk);
+    if (l > di.lds_max)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule needs %zu bytes of LDS, the device allows %zu", l, di.lds_max);
+    return 0;
+}
+
+MvLauncher mv_launcher(int t) {
+    switch (t) {
+    case kF16: return launch_mv_f16;
+    case kQ8_0: return launch_mv_q8_0;
+    case kQ4K: return launch_mv_q4_k;
+    case kQ6K: return launch_mv_q6_k;
+    default: return launch_mv_q5_0;
+    }
+}
+
+DqLauncher dq_launcher(int t) {
+    switch (t) {
+    case kF16: return launch_dq_f16;
+    case kQ8_0: return launch_dq_q8_0;
+    case kQ4K: return launch_dq_q4_k;
+    case kQ6K: return launch_dq_q6_k;
+    default: return launch_dq_q5_0;
+    }
+}
+
+int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+        const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream) {
+    g_err.clear();
+    const row_exact_strides_t s = resolve_strides(strides, m, n, k);
+    uint64_t wb, xbytes, ybytes;
+    int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes);
+    if (rc) return rc;
+    if (pin) {
+        rc = check_schedule_fields(t, k, *pin);
+        if (rc) return rc;
+    }
+    DevInfo di;
+    rc = device_info(di);
+    if (rc) return rc;
+    row_exact_schedule_t sch;
+    if (pin) {
+        sch = *pin;
+    } else {
+        rc = default_schedule(t, n, k, m, batch, sch);
+        if (rc) return rc;
+    }
+    rc = check_schedule_fields(t, k, sch);
+    if (!rc) rc = check_schedule_device(t, k, m, sch, di);
+    if (rc) return rc;
+
+    MvArgs a;
+    a.W = (const uint8_t *)W;
+    a.x = x;
+    a.y = y;
+    a.row_bytes = row_bytes_of(t, k);
+    a.batch_bytes = a.row_bytes * n;
+    a.xbs = s.x_batch_stride;
+    a.ybs = s.y_batch_stride;
+    a.n = n;
+    a.k = k;
+    a.xrs = s.x_row_stride;
+    a.yrs = s.y_row_stride;
+    a.pieces = pieces_of(t, k);
+    const uint32_t nr = sch.rows_per_wave;
+    a.groups_per_batch = (n + nr - 1) / nr;
+    uint32_t wgs = sch.workgroups_per_batch < a.groups_per_batch ? sch.workgroups_per_batch : a.groups_per_batch;
+    a.groups_per_wg = (a.groups_per_batch + wgs - 1) / wgs;
+    wgs = (a.groups_per_batch + a.groups_per_wg - 1) / a.groups_per_wg;  // as the kernel recomputes it
+    const uint32_t step = wave_step_values(t);
+    if (sch.k_chunk >= k) {
+        a.nchunks = 1;
+        a.kchunk = k;
+        a.pieces_per_chunk = a.pieces;
+    } else {
+        a.kchunk = sch.k_chunk;
+        a.pieces_per_chunk = sch.k_chunk / step * 64;
+        a.nchunks = (a.pieces + a.pieces_per_chunk - 1) / a.pieces_per_chunk;
+    }
+    a.xs_stride = xs_stride(t, a.kchunk);
+    const uint64_t grid_x = (uint64_t)wgs * batch;
+    if (grid_x > 0x7fffffffull)
+        return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);
+    const size_t lds = lds_bytes(t, m, k, sch.k_chunk);
+    hipError_t e = mv_launcher(t)(a, m, nr, dim3((uint32_t)grid_x), dim3(64 * sch.waves_per_workgroup), lds, stream);
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int row_exact_mv(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m,
+                 uint32_t batch, const row_exact_strides_t *strides, hipStream_t stream) {
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream);
+}
+
+int row_exact_mv_scheduled(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n, uint32_t k,
+                           uint32_t m, uint32_t batch, const row_exact_strides_t *strides,
+                           const row_exact_schedule_t *schedule, hipStream_t stream) {
+    if (!schedule) {
+        g_err.clear();
+        return fail(ROW_EXACT_ESCHEDULE, "schedule must be non-NULL");
+    }
+    return run((int)wt, W, x, y, n, k, m, batch, strides, schedule, stream);
+}
+
+int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                       row_exact_schedule_t *out) {
+    g_err.clear();
+    int rc = check_shape((int)wt, n, k, m, batch);
+    if (rc) return rc;
+    if (!out) return fail(ROW_EXACT_EARG, "out must be non-NULL");
+    return default_schedule((int)wt, n, k, m, batch, *out);
+}
+
+uint64_t row_exact_row_bytes(row_exact_weight_t wt, uint32_t k) {
+    return valid_type((int)wt) ? row_bytes_of((int)wt, k) : 0;
+}
+
+int row_exact_required_bytes(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                             const row_exact_strides_t *strides, uint64_t *w_bytes, uint64_t *x_bytes,
+                             uint64_t *y_bytes) {
+    g_err.clear();
+    int rc = check_shape((int)wt, n, k, m, batch);
+    if (rc) return rc;
+    const row_exact_strides_t s = resolve_strides(strides, m, n, k);
+    uint64_t wb, xb, yb;
+    rc = sizes((int)wt, n, k, m, batch, s, wb, xb, yb);
+    if (rc) return rc;
+    if (w_bytes) *w_bytes = wb;
+    if (x_bytes) *x_bytes = xb;
+    if (y_bytes) *y_bytes = yb;
+    return 0;
+}
+
+int row_exact_dequant(row_exact_weight_t wt, const void *W, float *out, uint32_t rows, uint32_t k,
+                      hipStream_t stream) {
+    g_err.clear();
+    const int t = (int)wt;
+    int rc = check_shape(t, rows, k, 1, 1);
+    if (rc) return rc;
+    if (!W || !out) return fail(ROW_EXACT_EARG, "W and out must be non-NULL device pointers");
+    if ((uintptr_t)W % w_align(t) || (uintptr_t)out % 4)
+        return fail(ROW_EXACT_EALIGN, "weight pointer must be %u-byte and out 4-byte aligned", w_align(t));
+    const u128 wb = (u128)row_bytes_of(t, k) * rows;
+    const u128 ob = (u128)rows * k * 4;
+    if (wb >= ((u128)1 << 62) || ob >= ((u128)1 << 62))
+        return fail(ROW_EXACT_EEXTENT, "operand sizes overflow 64-bit byte offsets");
+    if (overlap((uintptr_t)out, (uint64_t)ob, (uintptr_t)W, (uint64_t)wb))
+        return fail(ROW_EXACT_EALIAS, "output range overlaps the weight range");
+    DqArgs a;
+    a.W = (const uint8_t *)W;
+    a.out = out;
+    a.row_bytes = row_bytes_of(t, k);
+    a.rows = rows;
+    a.k = k;
+    a.pieces = pieces_of(t, k);
+    if ((uint64_t)a.rows * a.pieces / 256 >= 0x7fffffffull)
+        return fail(ROW_EXACT_EEXTENT, "too many rows for one launch");
+    hipError_t e = dq_launcher(t)(a, stream);
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    return 0;
+}
+
+const char *row_exact_last_error(void) { return g_err.c_str(); }
+
+uint64_t row_exact_launch_count(void) { return g_launches.load(std::memory_order_relaxed); }
+
+}  // extern "C"

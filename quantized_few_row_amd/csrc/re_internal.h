@@ -1,0 +1,105 @@
+// Host/device shared definitions of the row-exact mat-vec library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rex {
+
+enum WeightType : int { kF16 = 0, kQ8_0 = 1, kQ4K = 2, kQ6K = 3, kQ5_0 = 4 };
+
+// Kernel argument block (passed by value).
+struct MvArgs {
+    const uint8_t *W;
+    const float *x;
+    float *y;
+    uint64_t row_bytes;    // bytes per weight row
+    uint64_t batch_bytes;  // n * row_bytes
+    uint64_t xbs, ybs;     // batch strides (elements)
+    uint32_t n, k;
+    uint32_t xrs, yrs;     // row strides (elements)
+    uint32_t pieces;            // per-lane work items per weight row
+    uint32_t groups_per_batch;  // ceil(n / rows_per_wave)
+    uint32_t groups_per_wg;     // row groups one workgroup handles
+    uint32_t nchunks;           // LDS passes over K
+    uint32_t pieces_per_chunk;  // multiple of 64 (one wave step)
+    uint32_t kchunk;            // values per pass
+    uint32_t xs_stride;         // floats per staged x row in LDS (padded)
+};
+
+struct DqArgs {
+    const uint8_t *W;
+    float *out;
+    uint64_t row_bytes;
+    uint32_t rows, k, pieces;
+};
+
+// Per-type static geometry, shared by host (schedule) and device (kernels).
+template <int T> struct Geo;
+template <> struct Geo<kF16> {   // piece: 8 consecutive halves (16 bytes)
+    static constexpr int PV = 8, NG = 2, PADP = 32;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return (k + 7) / 8; }
+};
+template <> struct Geo<kQ8_0> {  // piece: one 34-byte block
+    static constexpr int PV = 32, NG = 8, PADP = 32;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 32; }
+};
+template <> struct Geo<kQ4K> {   // piece: 16 nibble bytes of a super-block (32 values)
+    static constexpr int PV = 32, NG = 8, PADP = 64;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 256 * 8; }
+};
+template <> struct Geo<kQ6K> {   // piece: a quarter super-block (64 values)
+    static constexpr int PV = 64, NG = 16, PADP = 128;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 256 * 4; }
+};
+template <> struct Geo<kQ5_0> {  // piece: one 22-byte block
+    static constexpr int PV = 32, NG = 8, PADP = 32;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 32; }
+};
+
+// Values covered by one wave step (64 pieces).
+inline uint32_t wave_step_values(int t) {
+    switch (t) {
+    case kF16: return 64 * Geo<kF16>::PV;
+    case kQ8_0: return 64 * Geo<kQ8_0>::PV;
+    case kQ4K: return 64 * Geo<kQ4K>::PV;
+    case kQ6K: return 64 * Geo<kQ6K>::PV;
+    default: return 64 * Geo<kQ5_0>::PV;
+    }
+}
+inline uint32_t pieces_of(int t, uint32_t k) {
+    switch (t) {
+    case kF16: return Geo<kF16>::pieces(k);
+    case kQ8_0: return Geo<kQ8_0>::pieces(k);
+    case kQ4K: return Geo<kQ4K>::pieces(k);
+    case kQ6K: return Geo<kQ6K>::pieces(k);
+    default: return Geo<kQ5_0>::pieces(k);
+    }
+}
+inline uint32_t pad_period(int t) {
+    switch (t) {
+    case kF16: return Geo<kF16>::PADP;
+    case kQ8_0: return Geo<kQ8_0>::PADP;
+    case kQ4K: return Geo<kQ4K>::PADP;
+    case kQ6K: return Geo<kQ6K>::PADP;
+    default: return Geo<kQ5_0>::PADP;
+    }
+}
+
+// Launchers, one translation unit per weight type.
+typedef hipError_t (*MvLauncher)(const MvArgs &, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds,
+                                 hipStream_t s);
+typedef hipError_t (*DqLauncher)(const DqArgs &, hipStream_t s);
+
+hipError_t launch_mv_f16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_q8_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_q4_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_q6_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_q5_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_dq_f16(const DqArgs &, hipStream_t);
+hipError_t launch_dq_q8_0(const DqArgs &, hipStream_t);
+hipError_t launch_dq_q4_k(const DqArgs &, hipStream_t);
+hipError_t launch_dq_q6_k(const DqArgs &, hipStream_t);
+hipError_t launch_dq_q5_0(const DqArgs &, hipStream_t);
+
+}  // namespace rex

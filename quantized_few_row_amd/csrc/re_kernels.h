@@ -1,0 +1,614 @@
+// Device code of the row-exact few-row mat-vec (gfx950, wave64).
+//
+// Product (mlx-native 0.18.0, src/ops/row_exact_matvec.rs, module docs):
+//   y[b][j][i] = sum_kk W[b*n + i][kk] * x[b][j][kk],  1 <= m <= 8.
+//
+// Work decomposition
+//   - A weight row is cut into "pieces": per-lane work items whose bytes sit
+//     together in the row (F16: 8 values; Q8_0 / Q5_0: one block; Q4_K: 16
+//     nibble bytes of a super-block; Q6_K: a quarter super-block).  Lane L of
+//     the wave owning the row takes pieces L, L+64, L+128, ... in that order,
+//     so each load instruction of a wave covers adjacent bytes of the row.
+//   - A wave streams rows_per_wave (NR) rows at once: every input value read
+//     from LDS feeds NR weight rows ("nr0 rows sharing each input load").
+//   - The m input rows of the batch are staged once per pass into LDS
+//     (padded so that the lanes' 16-byte reads hit distinct banks).
+//
+// Numerics (module docs, "Row exactness")
+//   - Every weight is decoded to its exact float32 value in registers (Q4_K's
+//     value is one rounding of an exact difference, via fma).
+//   - For each (row, input row) a lane keeps one accumulator and folds its
+//     pieces' products into it with an explicit fmaf chain, in piece order
+//     and, inside a piece, in a fixed value order.  Nothing about that chain
+//     depends on m or on the packing (NR, waves per workgroup, grid).
+//   - The 64 lane partials of an output are added by one fixed tree: lanes
+//     (L, L^32), then (L, L^16), then within each row of 16 lanes: rotate-8,
+//     half-row mirror, xor 2, xor 1.  The first two levels are done with the
+//     gfx950 permlane32/permlane16 swaps and, when a lane holds several
+//     outputs, transposed (each swap hands half of the outputs to the other
+//     half of the wave, so no work is duplicated); the rest with DPP.  IEEE
+//     addition is commutative, so whichever lane performs a given pairwise
+//     add produces the same bits: every output gets the same tree for every
+//     m and every packing.
+#pragma once
+
+#include "re_internal.h"
+
+namespace rex {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x3a4 __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Exact widening of an IEEE half (subnormals included).
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// ({hi, lo} >> 8*sh)[31:0]
+__device__ __forceinline__ uint32_t abyte(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+
+// Loads below take a wave-uniform row base R (4-byte aligned; 16-byte for
+// Q4_K, 8-byte for F16) and a per-lane 32-bit byte offset, so they compile
+// to global loads with a scalar base.
+template <class V> __device__ __forceinline__ V ldv(const uint8_t *R, uint32_t off) {
+    return *(const V *)(R + off);
+}
+__device__ __forceinline__ uint32_t ld16(const uint8_t *R, uint32_t off) { return *(const uint16_t *)(R + off); }
+
+// 16 bytes at an even offset o (R + o - 2 is readable when o % 4 == 2).  Reads
+// the aligned dwords around it and the last two bytes with a 16-bit load, so
+// nothing past R + o + 16 is touched.
+__device__ __forceinline__ void load16_a2(const uint8_t *R, uint32_t o, uint32_t (&out)[4]) {
+    const uint32_t sh = o & 3u;
+    const u32x4a4 r = ldv<u32x4a4>(R, o - sh);
+    const uint32_t t = ld16(R, o + 14);
+    out[0] = abyte(r.y, r.x, sh);
+    out[1] = abyte(r.z, r.y, sh);
+    out[2] = abyte(r.w, r.z, sh);
+    out[3] = abyte(t, r.w, sh);
+}
+
+template <int T> struct Tr;
+
+// Each Tr<T> gives, for piece p of a row:
+//   load(R, o0, p)  raw bytes (o0 = offset of the row from R)
+//   prep(raw, p)    per-piece scales
+//   deq(raw, pre, g, w)  exact float32 values of the piece's group g (4 values)
+//   vpos(p, g)      index in the row of the group's first value
+//   xoff(p) + goff(g) == vpos(p, g) - vb padded for LDS (xoff relative to the
+//                   pass's first value vb, which is a wave-step multiple)
+
+// ---------------------------------------------------------------- F16
+// Piece p: values 8p..8p+7 (16 bytes).  k % 8 == 4 leaves a half piece.
+template <> struct Tr<kF16> : Geo<kF16> {
+    struct Raw { uint32_t w[4]; };
+    struct Pre {};
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t k) {
+        Raw r;
+        const uint32_t o = o0 + 16 * p;
+        if (8 * p + 8 <= k) {
+            const u32x4a4 v = ldv<u32x4a4>(R, o);
+            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+        } else {
+            const u32x2a4 v = ldv<u32x2a4>(R, o);
+            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = 0; r.w[3] = 0;
+        }
+        return r;
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &, uint32_t) { return {}; }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &, int g, float (&w)[4]) {
+        w[0] = h2f(r.w[2 * g] & 0xffffu);
+        w[1] = h2f(r.w[2 * g] >> 16);
+        w[2] = h2f(r.w[2 * g + 1] & 0xffffu);
+        w[3] = h2f(r.w[2 * g + 1] >> 16);
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 8 * p + 4 * g; }
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
+        const uint32_t q = p - vb / 8;
+        return 8 * q + 4 * (q / 4);
+    }
+    static constexpr uint32_t goff(int g) { return 4 * g; }
+    static __device__ __forceinline__ bool group_valid(uint32_t p, int g, uint32_t k) {
+        return g == 0 || 8 * p + 4 < k;
+    }
+};
+
+// ---------------------------------------------------------------- Q8_0
+// Piece p: block p (34 bytes: f16 d, 32 int8).  w = d * q.
+template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
+    struct Raw { uint32_t q[8]; uint32_t d; };
+    struct Pre { float d; };
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        Raw r;
+        const uint32_t B = o0 + 34 * p;
+        r.d = ld16(R, B);
+        const uint32_t F = B + 2;  // quants
+        const uint32_t sh = F & 3u;
+        const u32x4a4 r0 = ldv<u32x4a4>(R, F - sh), r1 = ldv<u32x4a4>(R, F - sh + 16);
+        const uint32_t t = ld16(R, F + 30);
+        const uint32_t W9[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, t};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.q[i] = abyte(W9[i + 1], W9[i], sh);
+        return r;
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d)}; }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pr.d * (float)(int8_t)(r.q[g] >> (8 * i));
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 32 * p + 4 * g; }
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) { return 36 * (p - vb / 32); }
+    static constexpr uint32_t goff(int g) { return 4 * g; }
+    static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
+};
+
+// ---------------------------------------------------------------- Q5_0
+// Piece p: block p (22 bytes: f16 d, u32 high bits, 16 nibble bytes).
+// Value i < 16: low nibble of byte i; i >= 16: high nibble of byte i - 16;
+// bit i of the high bits is bit 4.  w = d * (q - 16).
+template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
+    struct Raw { uint32_t qs[4]; uint32_t qh; uint32_t d; };
+    struct Pre { float d; };
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        Raw r;
+        const uint32_t B = o0 + 22 * p;
+        const uint32_t sh = B & 3u;
+        const u32x3a4 e = ldv<u32x3a4>(R, B - sh);  // covers bytes 0..7 of the block
+        const uint32_t b0 = abyte(e.y, e.x, sh);     // d | qh.lo << 16
+        const uint32_t b1 = abyte(e.z, e.y, sh);     // qh.hi | qs[0..1] << 16
+        r.d = b0 & 0xffffu;
+        r.qh = abyte(b1, b0, 2);
+        load16_a2(R, B + 6, r.qs);
+        return r;
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d)}; }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+        const uint32_t dw = r.qs[g & 3];
+        const int nsh = g >= 4 ? 4 : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (dw >> (8 * i + nsh)) & 15u;
+            const uint32_t hb = (r.qh >> (4 * g + i)) & 1u;
+            w[i] = pr.d * (float)((int)(lo | (hb << 4)) - 16);
+        }
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 32 * p + 4 * g; }
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) { return 36 * (p - vb / 32); }
+    static constexpr uint32_t goff(int g) { return 4 * g; }
+    static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
+};
+
+// ---------------------------------------------------------------- Q4_K
+// Piece p: super-block p/8, nibble bytes 16q..16q+15 (q = p % 8) of its 128;
+// they hold chunk c = q/2: low nibbles are values 64c + 16(q%2) + 0..15 of
+// sub-block 2c, high nibbles values 64c + 32 + 16(q%2) + 0..15 of sub-block
+// 2c+1.  w = fma(d*sc, q, -(dmin*mn)): one rounding of the exact value.
+template <> struct Tr<kQ4K> : Geo<kQ4K> {
+    struct Raw { uint32_t qs[4]; uint32_t h[4]; };
+    struct Pre { float dsc[2], dmn[2]; };
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        Raw r;
+        const uint32_t B = o0 + 144 * (p >> 3);
+        const u32x4 hv = ldv<u32x4>(R, B);
+        const u32x4 qv = ldv<u32x4>(R, B + 16 + 16 * (p & 7));
+        r.h[0] = hv.x; r.h[1] = hv.y; r.h[2] = hv.z; r.h[3] = hv.w;
+        r.qs[0] = qv.x; r.qs[1] = qv.y; r.qs[2] = qv.z; r.qs[3] = qv.w;
+        return r;
+    }
+    // 6-bit scale and min of sub-block s from the 12 packed bytes
+    // (h[1] = bytes 0..3, h[2] = bytes 4..7, h[3] = bytes 8..11).
+    static __device__ __forceinline__ void scale_min(const uint32_t (&h)[4], uint32_t s, uint32_t &sc,
+                                                     uint32_t &mn) {
+        if (s < 4) {
+            sc = (h[1] >> (8 * s)) & 63u;
+            mn = (h[2] >> (8 * s)) & 63u;
+        } else {
+            const uint32_t u = 8 * (s - 4);
+            sc = ((h[3] >> u) & 15u) | (((h[1] >> (u + 6)) & 3u) << 4);
+            mn = ((h[3] >> (u + 4)) & 15u) | (((h[2] >> (u + 6)) & 3u) << 4);
+        }
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t p) {
+        Pre pr;
+        const float d = h2f(r.h[0] & 0xffffu), dmin = h2f(r.h[0] >> 16);
+        const uint32_t s0 = ((p & 7) >> 1) * 2;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            uint32_t sc, mn;
+            scale_min(r.h, s0 + e, sc, mn);
+            pr.dsc[e] = d * (float)sc;     // exact
+            pr.dmn[e] = dmin * (float)mn;  // exact
+        }
+        return pr;
+    }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+        const int e = g >= 4 ? 1 : 0;
+        const uint32_t dw = r.qs[g & 3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = __builtin_fmaf(pr.dsc[e], (float)((dw >> (8 * i + 4 * e)) & 15u), -pr.dmn[e]);
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) {
+        const uint32_t q = p & 7;
+        return 256 * (p >> 3) + 64 * (q >> 1) + 16 * (q & 1) + (g >= 4 ? 32 : 0) + 4 * (g & 3);
+    }
+    // PADP 64: pad index = 4*(super-block) + chunk
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
+        const uint32_t sb = (p >> 3) - vb / 256, q = p & 7;
+        return 272 * sb + 68 * (q >> 1) + 16 * (q & 1);
+    }
+    static constexpr uint32_t goff(int g) { return (g >= 4 ? 32 : 0) + 4 * (g & 3); }
+    static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
+};
+
+// ---------------------------------------------------------------- Q6_K
+// Piece p: super-block p/4, half hh = (p/2)%2, lane column block l0 = 16(p%2):
+// values 128hh + 32t + l0 + 0..15 for t = 0..3.  Low 4 bits from
+// ql[64hh + 32(t&1) + l] (low nibble for t < 2, high for t >= 2), high 2 bits
+// from bits 2t..2t+1 of qh[32hh + l], scale sc[8hh + 2t + l0/16].
+// w = (d * sc) * (q - 32), exact.
+template <> struct Tr<kQ6K> : Geo<kQ6K> {
+    struct Raw { uint32_t ql0[4], ql1[4], qh[4], sc[2], d; };
+    struct Pre { float ds[4]; };
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        Raw r;
+        const uint32_t hh = (p >> 1) & 1, l0 = 16 * (p & 1);
+        const uint32_t B = o0 + 210 * (p >> 2);
+        load16_a2(R, B + 64 * hh + l0, r.ql0);
+        load16_a2(R, B + 64 * hh + 32 + l0, r.ql1);
+        load16_a2(R, B + 128 + 32 * hh + l0, r.qh);
+        const uint32_t G = B + 192 + 8 * hh;  // sc[8hh .. 8hh+7]
+        const uint32_t sh = G & 3u;
+        const u32x2a4 v = ldv<u32x2a4>(R, G - sh);
+        const uint32_t t = ld16(R, G + 6);
+        r.sc[0] = abyte(v.y, v.x, sh);
+        r.sc[1] = abyte(t, v.y, sh);
+        r.d = ld16(R, B + 208);
+        return r;
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t p) {
+        Pre pr;
+        const float d = h2f(r.d);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t idx = 2 * t + (p & 1);
+            const int8_t s = (int8_t)(r.sc[idx >> 2] >> (8 * (idx & 3)));
+            pr.ds[t] = d * (float)s;  // exact
+        }
+        return pr;
+    }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+        const int t = g >> 2, G = g & 3;
+        const uint32_t ldw = (t & 1) ? r.ql1[G] : r.ql0[G];
+        const int nsh = t >= 2 ? 4 : 0;
+        const uint32_t hdw = r.qh[G];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (ldw >> (8 * i + nsh)) & 15u;
+            const uint32_t hi = (hdw >> (8 * i + 2 * t)) & 3u;
+            w[i] = pr.ds[t] * (float)((int)(lo | (hi << 4)) - 32);
+        }
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) {
+        return 256 * (p >> 2) + 128 * ((p >> 1) & 1) + 32 * (g >> 2) + 16 * (p & 1) + 4 * (g & 3);
+    }
+    // PADP 128: pad index = 2*(super-block) + hh
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
+        const uint32_t sb = (p >> 2) - vb / 256, hh = (p >> 1) & 1;
+        return 264 * sb + 132 * hh + 16 * (p & 1);
+    }
+    static constexpr uint32_t goff(int g) { return 32 * (g >> 2) + 4 * (g & 3); }
+    static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
+};
+
+// ---------------------------------------------------------------- reduction
+
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Lanes (L, L^32): X keeps lanes 0..31 of X and receives Y's lanes 0..31 in
+// its upper half; Y receives X's upper half in its lower half.  X' + Y' is
+// X[L] + X[L+32] on lanes 0..31 and Y[L-32] + Y[L] on lanes 32..63.
+__device__ __forceinline__ float swap32_add(float x, float y) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// Lanes (L, L^16): rows 0 and 2 get X's row pair sum, rows 1 and 3 Y's.
+__device__ __forceinline__ float swap16_add(float x, float y) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+constexpr int pow2ceil(int v) { return v <= 1 ? 1 : 2 * pow2ceil((v + 1) / 2); }
+
+// Sum each of the NR*M accumulators over the 64 lanes with the fixed tree
+// and store output (r, j) to y[j*yrs + row0 + r] when row0 + r < n.
+template <int M, int NR>
+__device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *__restrict__ yb, uint32_t yrs,
+                                             uint32_t n, uint32_t row0, uint32_t lane) {
+    constexpr int NA = NR * M;
+    constexpr int A = pow2ceil(NA);
+    float v[A];
+#pragma unroll
+    for (int a = 0; a < A; ++a) v[a] = a < NA ? acc[a / M][a % M] : 0.0f;
+
+    // level 1: (L, L^32)
+    constexpr int A1 = A >= 2 ? A / 2 : 1;
+    if constexpr (A >= 2) {
+#pragma unroll
+        for (int a = 0; a < A1; ++a) v[a] = swap32_add(v[a], v[a + A1]);
+    } else {
+        v[0] = swap32_add(v[0], v[0]);
+    }
+    // level 2: (L, L^16)
+    constexpr int A2 = A1 >= 2 ? A1 / 2 : 1;
+    if constexpr (A1 >= 2) {
+#pragma unroll
+        for (int a = 0; a < A2; ++a) v[a] = swap16_add(v[a], v[a + A2]);
+    } else {
+        v[0] = swap16_add(v[0], v[0]);
+    }
+    // levels 3..6 inside each row of 16 lanes
+#pragma unroll
+    for (int a = 0; a < A2; ++a) {
+        v[a] = v[a] + dpp_mov<0x128>(v[a]);  // row_ror:8     (L, L^8)
+        v[a] = v[a] + dpp_mov<0x141>(v[a]);  // row_half_mirror (L, 7-L)
+        v[a] = v[a] + dpp_mov<0x4E>(v[a]);   // quad_perm 2,3,0,1
+        v[a] = v[a] + dpp_mov<0xB1>(v[a]);   // quad_perm 1,0,3,2
+    }
+
+    // Which lanes hold which outputs: A >= 4: row R = lane/16 holds outputs
+    // R*A2 + a; A == 2: lanes 0..31 output 0, lanes 32..63 output 1; A == 1:
+    // every lane output 0.
+    uint32_t base;
+    bool holder;
+    if constexpr (A >= 4) {
+        holder = (lane & 15) == 0;
+        base = (lane >> 4) * A2;
+    } else if constexpr (A == 2) {
+        holder = (lane & 31) == 0;
+        base = lane >> 5;
+    } else {
+        holder = lane == 0;
+        base = 0;
+    }
+    if (holder) {
+#pragma unroll
+        for (int a = 0; a < A2; ++a) {
+            const uint32_t o = base + a;
+            if (o < (uint32_t)NA) {
+                const uint32_t r = o / M, j = o % M;
+                if (row0 + r < n) yb[(uint64_t)j * yrs + row0 + r] = v[a];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- x staging
+
+template <int T, int M>
+__device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
+                                        uint32_t v0, uint32_t v1, uint32_t XS) {
+    const uint32_t n4 = (v1 - v0) >> 2;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+        const float *src = xb + (uint64_t)j * xrs + v0;
+        float *dst = xs + j * XS;
+        for (uint32_t q = threadIdx.x; q < n4; q += blockDim.x) {
+            const uint32_t lv = q << 2;
+            *(f32x4 *)(dst + lv + 4 * (lv / Geo<T>::PADP)) = *(const f32x4 *)(src + lv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- one piece
+
+template <int T, int M, int NR>
+__device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typename Tr<T>::Raw (&raw)[NR], uint32_t p,
+                                              uint32_t vb, const float *__restrict__ xs, uint32_t XS, uint32_t k) {
+    using TR = Tr<T>;
+    typename TR::Pre pre[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) pre[r] = TR::prep(raw[r], p);
+    const float *__restrict__ xp = xs + TR::xoff(p, vb);
+#pragma unroll
+    for (int g = 0; g < TR::NG; ++g) {
+        if (!TR::group_valid(p, g, k)) continue;
+        f32x4 xv[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) xv[j] = *(const f32x4 *)(xp + j * XS + TR::goff(g));
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            float w[4];
+            TR::deq(raw[r], pre[r], g, w);
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[r][j] = __builtin_fmaf(w[i], xv[j][i], acc[r][j]);
+            }
+        }
+    }
+}
+
+// Pieces [pb, pe) of the NR rows, this lane's share (pb + lane, +64, ...),
+// with the next piece's loads issued before the current piece's math.
+template <int T, int M, int NR>
+__device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *const (&R)[NR],
+                                           const uint32_t (&o0)[NR], uint32_t pb, uint32_t pe, uint32_t vb,
+                                           const float *__restrict__ xs, uint32_t XS, uint32_t k, uint32_t lane) {
+    using TR = Tr<T>;
+    using Raw = typename TR::Raw;
+    uint32_t p = pb + lane;
+    if (p >= pe) return;
+    Raw A[NR], B[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) A[r] = TR::load(R[r], o0[r], p, k);
+    while (true) {
+        const uint32_t p1 = p + 64;
+        const bool m1 = p1 < pe;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) B[r] = TR::load(R[r], o0[r], m1 ? p1 : p, k);
+        compute_piece<T, M, NR>(acc, A, p, vb, xs, XS, k);
+        if (!m1) break;
+        const uint32_t p2 = p1 + 64;
+        const bool m2 = p2 < pe;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) A[r] = TR::load(R[r], o0[r], m2 ? p2 : p1, k);
+        compute_piece<T, M, NR>(acc, B, p1, vb, xs, XS, k);
+        if (!m2) break;
+        p = p2;
+    }
+}
+
+// Wave-uniform base (aligned down to 4 bytes) and byte offset of each row.
+template <int NR>
+__device__ __forceinline__ void row_bases(const uint8_t *Wb, uint64_t row_bytes, uint32_t n, uint32_t row0,
+                                          const uint8_t *(&R)[NR], uint32_t (&o0)[NR]) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const uint32_t row = min(row0 + r, n - 1);
+        const uint8_t *rp = Wb + (uint64_t)row * row_bytes;
+        const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
+        R[r] = rp - lo;
+        o0[r] = lo;
+    }
+}
+
+// ---------------------------------------------------------------- kernels
+
+template <int T, int M, int NR>
+__global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
+    extern __shared__ float xs[];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nwaves = blockDim.x >> 6;
+    const uint32_t wgs_per_batch = (a.groups_per_batch + a.groups_per_wg - 1) / a.groups_per_wg;
+    const uint32_t b = blockIdx.x / wgs_per_batch;  // batch-major flattening
+    const uint32_t w = blockIdx.x - b * wgs_per_batch;
+    const float *__restrict__ xb = a.x + b * a.xbs;
+    const uint8_t *__restrict__ Wb = a.W + b * a.batch_bytes;
+    float *__restrict__ yb = a.y + b * a.ybs;
+    const uint32_t g0 = w * a.groups_per_wg;
+    const uint32_t g1 = min(g0 + a.groups_per_wg, a.groups_per_batch);
+    const uint32_t XS = a.xs_stride;
+
+    if (a.nchunks == 1) {
+        stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
+        __syncthreads();
+        for (uint32_t g = g0 + wave; g < g1; g += nwaves) {
+            float acc[NR][M];
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int j = 0; j < M; ++j) acc[r][j] = 0.0f;
+            const uint8_t *R[NR];
+            uint32_t o0[NR];
+            row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
+            accumulate<T, M, NR>(acc, R, o0, 0, a.pieces, 0, xs, XS, a.k, lane);
+            reduce_store<M, NR>(acc, yb, a.yrs, a.n, g * NR, lane);
+        }
+    } else {
+        for (uint32_t base = g0; base < g1; base += nwaves) {
+            const uint32_t g = base + wave;
+            const bool active = g < g1;
+            float acc[NR][M];
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int j = 0; j < M; ++j) acc[r][j] = 0.0f;
+            const uint8_t *R[NR];
+            uint32_t o0[NR];
+            row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
+            for (uint32_t c = 0; c < a.nchunks; ++c) {
+                const uint32_t pb = c * a.pieces_per_chunk;
+                const uint32_t pe = min(pb + a.pieces_per_chunk, a.pieces);
+                const uint32_t vb = pb * Geo<T>::PV;
+                const uint32_t ve = min(a.k, vb + a.kchunk);
+                __syncthreads();
+                stage_x<T, M>(xs, xb, a.xrs, vb, ve, XS);
+                __syncthreads();
+                if (active) accumulate<T, M, NR>(acc, R, o0, pb, pe, vb, xs, XS, a.k, lane);
+            }
+            if (active) reduce_store<M, NR>(acc, yb, a.yrs, a.n, g * NR, lane);
+        }
+    }
+}
+
+// out[r*k + v] = weight v of row r, one thread per (row, piece).
+template <int T>
+__global__ void __launch_bounds__(256) dq_kernel(const DqArgs a) {
+    using TR = Tr<T>;
+    const uint64_t gid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (uint64_t)a.rows * a.pieces) return;
+    const uint32_t r = (uint32_t)(gid / a.pieces), p = (uint32_t)(gid % a.pieces);
+    const uint8_t *rp = a.W + (uint64_t)r * a.row_bytes;
+    const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
+    const typename TR::Raw raw = TR::load(rp - lo, lo, p, a.k);
+    const typename TR::Pre pre = TR::prep(raw, p);
+    float *o = a.out + (uint64_t)r * a.k;
+#pragma unroll
+    for (int g = 0; g < TR::NG; ++g) {
+        if (!TR::group_valid(p, g, a.k)) continue;
+        float w[4];
+        TR::deq(raw, pre, g, w);
+        const uint32_t v = TR::vpos(p, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[v + i] = w[i];
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int T, int M, int NR>
+hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    const void *fn = (const void *)mv_kernel<T, M, NR>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    MvArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(fn, grid, block, args, lds, s);
+}
+
+template <int T, int M>
+hipError_t launch_m(const MvArgs &a, uint32_t nr, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    switch (nr) {
+    case 1: return launch_one<T, M, 1>(a, grid, block, lds, s);
+    case 2: return launch_one<T, M, 2>(a, grid, block, lds, s);
+    case 4: return launch_one<T, M, 4>(a, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+hipError_t launch_mv(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    switch (m) {
+    case 1: return launch_m<T, 1>(a, nr, grid, block, lds, s);
+    case 2: return launch_m<T, 2>(a, nr, grid, block, lds, s);
+    case 3: return launch_m<T, 3>(a, nr, grid, block, lds, s);
+    case 4: return launch_m<T, 4>(a, nr, grid, block, lds, s);
+    case 5: return launch_m<T, 5>(a, nr, grid, block, lds, s);
+    case 6: return launch_m<T, 6>(a, nr, grid, block, lds, s);
+    case 7: return launch_m<T, 7>(a, nr, grid, block, lds, s);
+    case 8: return launch_m<T, 8>(a, nr, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+hipError_t launch_dq(const DqArgs &a, hipStream_t s) {
+    const uint64_t total = (uint64_t)a.rows * a.pieces;
+    const dim3 grid((uint32_t)((total + 255) / 256));
+    DqArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel((const void *)dq_kernel<T>, grid, dim3(256), args, 0, s);
+}
+
+}  // namespace rex

@@ -1,0 +1,198 @@
+"""C-ABI boundary on the CPU: the library loads, exports what the header
+declares, and rejects every invalid argument before touching the device.
+
+Calls here pass made-up device addresses; every one of them is invalid for
+another reason, so nothing is ever enqueued (validation runs before any HIP
+call).  The restated rules are those of mlx-native 0.18.0
+src/ops/row_exact_matvec.rs validate().
+"""
+import ctypes
+import glob
+import json
+import os
+import re
+
+import pytest
+
+import quantized_few_row_amd as qfr
+from quantized_few_row_amd import Schedule, Strides, Weight
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "page_constants.json")))
+
+# Made-up, well-aligned device addresses (never dereferenced).
+WP, XP, YP = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(row_exact_[a-z_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qfr.load_library()
+    declared = _declared_functions()
+    assert len(declared) == 8, declared
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_binding_names_mirror_the_abi():
+    for name in _declared_functions():
+        assert callable(getattr(qfr, name)), name
+
+
+def test_row_bytes_match_page():
+    for name, blk in GOLDEN["blocks"].items():
+        if name.startswith("_"):
+            continue
+        for nb in (1, 3, 16, 56):
+            assert qfr.row_exact_row_bytes(Weight[name], blk["values"] * nb) == blk["bytes"] * nb
+    assert qfr.row_exact_row_bytes(Weight.F16, 512) == 1024
+    assert qfr.row_exact_row_bytes(7, 512) == 0
+
+
+def test_weight_order_matches_page():
+    assert [w.name for w in Weight] == GOLDEN["weight_type_order"]["value"]
+    assert qfr.MAX_ROWS == GOLDEN["max_rows"]["value"]
+
+
+def test_stride_helpers_match_page_examples():
+    g = GOLDEN["grouped_token_major_example"]
+    s = qfr.grouped_token_major(g["m"], g["groups"], g["n"], g["k"])
+    assert s.astuple() == tuple(g["strides"][f] for f in ("x_row_stride", "x_batch_stride", "y_row_stride",
+                                                            "y_batch_stride"))
+    c = GOLDEN["contiguous_example"]
+    s = qfr.contiguous(c["m"], c["n"], c["k"])
+    assert s.astuple() == tuple(c["strides"][f] for f in ("x_row_stride", "x_batch_stride", "y_row_stride",
+                                                            "y_batch_stride"))
+
+
+def test_required_bytes_is_strided_extent():
+    # contiguous: W rows * row_bytes, x m*k floats, y m*n floats
+    w, x, y = qfr.row_exact_required_bytes(Weight.Q8_0, 4096, 4096, 8, 1)
+    assert (w, x, y) == (4096 * 4352, 8 * 4096 * 4, 8 * 4096 * 4)
+    g = GOLDEN["grouped_token_major_example"]
+    s = qfr.grouped_token_major(g["m"], g["groups"], g["n"], g["k"])
+    w, x, y = qfr.row_exact_required_bytes(Weight.Q5_0, g["n"], g["k"], g["m"], g["groups"], s)
+    # last element + 1: (batch-1)*bs + (m-1)*rs + cols
+    assert x == 4 * ((g["groups"] - 1) * g["k"] + (g["m"] - 1) * g["groups"] * g["k"] + g["k"])
+    assert y == 4 * ((g["groups"] - 1) * g["n"] + (g["m"] - 1) * g["groups"] * g["n"] + g["n"])
+    assert x == 4 * g["m"] * g["groups"] * g["k"] and y == 4 * g["m"] * g["groups"] * g["n"]
+    assert w == g["groups"] * g["n"] * (g["k"] // 32) * 22
+
+
+def _mv(wt=Weight.Q8_0, W=WP, x=XP, y=YP, n=64, k=256, m=4, batch=1, strides=None, schedule=None):
+    lib = qfr.load_library()
+    sp = ctypes.byref(strides) if strides is not None else None
+    if schedule is None:
+        rc = lib.row_exact_mv(int(wt), W, x, y, n, k, m, batch, sp, None)
+    else:
+        rc = lib.row_exact_mv_scheduled(int(wt), W, x, y, n, k, m, batch, sp, ctypes.byref(schedule), None)
+    return rc, qfr.row_exact_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(m=0), -1, "m (0) must be in 1..=8"),
+    (dict(m=9), -1, "m (9) must be in 1..=8"),
+    (dict(n=0), -1, "must be > 0"),
+    (dict(k=0), -1, "must be > 0"),
+    (dict(batch=0), -1, "must be > 0"),
+    (dict(wt=5), -1, "unknown weight type"),
+    (dict(wt=Weight.Q8_0, k=48), -1, "multiple of 32"),
+    (dict(wt=Weight.Q4_K, k=512 + 32), -1, "multiple of 256"),
+    (dict(wt=Weight.Q6_K, k=128), -1, "multiple of 256"),
+    (dict(wt=Weight.Q5_0, k=16), -1, "multiple of 32"),
+    (dict(wt=Weight.F16, k=6), -1, "multiple of 4"),
+    (dict(W=0), -1, "non-NULL"),
+    (dict(y=0), -1, "non-NULL"),
+    (dict(x=XP + 4), -2, "16-byte aligned"),
+    (dict(strides=Strides(258, 0, 64, 0)), -3, "multiples of 4"),
+    (dict(strides=Strides(256, 2, 64, 0), batch=2), -3, "multiples of 4"),
+    (dict(wt=Weight.Q4_K, W=WP + 4), -2, "16-byte"),
+    (dict(wt=Weight.F16, W=WP + 4, k=64), -2, "8-byte"),
+    (dict(wt=Weight.Q8_0, W=WP + 2), -2, "4-byte"),
+    (dict(y=YP + 2), -2, "4-byte aligned"),
+])
+def test_invalid_arguments(kw, code, text):
+    before = qfr.row_exact_launch_count()
+    rc, msg = _mv(**kw)
+    assert rc == code, (rc, msg)
+    assert msg.startswith("row_exact_mv: ") and text in msg, msg
+    assert qfr.row_exact_launch_count() == before
+
+
+@pytest.mark.parametrize("m,n,batch,s,ok", [
+    # batch 1: rows need y_row_stride >= n (or m == 1)
+    (4, 64, 1, Strides(256, 0, 63, 0), False),
+    (1, 64, 1, Strides(256, 0, 0, 0), None),
+    # m == 1, batch > 1: batches need y_batch_stride >= n
+    (1, 64, 3, Strides(256, 256, 0, 63), False),
+    # y_row_stride >= y_batch_stride: token-major, rows span every batch
+    (2, 64, 3, Strides(256, 256, 191, 64), False),
+    (2, 64, 3, Strides(256, 256, 192, 63), False),
+    # y_batch_stride > y_row_stride: batch-major
+    (3, 64, 2, Strides(256, 1024, 64, 191), False),
+    (3, 64, 2, Strides(256, 1024, 63, 1000), False),
+])
+def test_output_alias_rules(m, n, batch, s, ok):
+    # ok=None marks shapes that are valid: they are not called here (a valid
+    # call would reach the device); only the rejected ones are exercised.
+    if ok is None:
+        return
+    rc, msg = _mv(m=m, n=n, batch=batch, strides=s)
+    assert rc == -4 and "output strides overlap" in msg, msg
+
+
+def test_output_must_not_overlap_inputs():
+    rc, msg = _mv(y=WP + 64)
+    assert rc == -4 and "overlaps" in msg
+    rc, msg = _mv(y=XP + 1024)
+    assert rc == -4 and "overlaps" in msg
+
+
+@pytest.mark.parametrize("sched,text", [
+    (Schedule(2, 1, 8, 1, 1 << 30), "k_split"),
+    (Schedule(1, 3, 8, 1, 1 << 30), "rows_per_wave"),
+    (Schedule(1, 1, 0, 1, 1 << 30), "waves_per_workgroup"),
+    (Schedule(1, 1, 9, 1, 1 << 30), "waves_per_workgroup"),
+    (Schedule(1, 1, 8, 0, 1 << 30), "workgroups_per_batch"),
+    (Schedule(1, 1, 8, 4, 1000), "k_chunk"),
+])
+def test_invalid_schedule(sched, text):
+    rc, msg = _mv(k=4096, schedule=sched)
+    assert rc == -6 and text in msg, msg
+
+
+def test_null_schedule():
+    lib = qfr.load_library()
+    rc = lib.row_exact_mv_scheduled(1, WP, XP, YP, 64, 256, 4, 1, None, None, None)
+    assert rc == -6
+
+
+def test_extent_overflow():
+    # x extent (batch-1)*xbs + (m-1)*xrs + k in bytes beyond 2^62
+    rc, msg = _mv(n=64, k=256, m=8, batch=0xFFFFFFFF,
+                  strides=Strides(0xFFFFFFFC, 0xFFFFFFFC, 64, 0xFFFFFFFF))
+    assert rc == -5, msg
+
+
+def test_dequant_validation():
+    lib = qfr.load_library()
+    assert lib.row_exact_dequant(1, WP, YP, 0, 64, None) == -1
+    assert lib.row_exact_dequant(1, WP, YP, 4, 40, None) == -1
+    assert lib.row_exact_dequant(2, WP + 4, YP, 4, 256, None) == -2
+    assert lib.row_exact_dequant(1, WP, WP + 8, 4, 64, None) == -4
+    assert lib.row_exact_dequant(9, WP, YP, 4, 64, None) == -1
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(qfr, "_lib", None)
+    monkeypatch.setattr(qfr, "_LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(qfr.LibraryMissing):
+        qfr.row_exact_row_bytes(1, 32)

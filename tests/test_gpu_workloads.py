@@ -1,0 +1,73 @@
+"""The five synthetic workloads at full size, in the launch configuration the
+benchmark times (the default schedule).  The oracle checks sampled output
+rows (first, last and seeded random ones) and sampled weight rows; row
+exactness and repeatability are checked on every output, GPU against GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_few_row_amd as qfr
+import workloads as wl
+from gpu_util import bits, check_tolerance, oracle_sampled, run_mv, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = [w.name for w in wl.WORKLOADS]
+
+
+def _sample_rows(n, count=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, n // 2, n - 2, n - 1}
+    rows |= set(rng.integers(0, n, count).tolist())
+    return sorted(r for r in rows if 0 <= r < n)
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_workload(name):
+    w = wl.get(name)
+    t, n, k, batch = w.wtype, w.n, w.k, w.batch
+    print(f"[workload] {name}: type {wl.TYPE_NAMES[t]} n={n} k={k} batch={batch} m={w.ms}", flush=True)
+    W = w.make_weights()
+    x = w.make_x(8)
+    Wd = to_dev(W.ravel())
+    xd = to_dev(x.ravel())
+    rows = _sample_rows(n, seed=w.index)
+    rb = qfr.row_exact_row_bytes(t, k)
+
+    # dequantized weights, sampled rows, bit-exact
+    for r in rows[:8]:
+        out = torch.empty((1, k), dtype=torch.float32, device="cuda:0")
+        qfr.row_exact_dequant(t, Wd.data_ptr() + r * rb, out, 1, k)
+        torch.cuda.synchronize()
+        ref = oracle.dequant(t, W.ravel()[r * rb:(r + 1) * rb], 1, k)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), f"weight row {r}"
+
+    xrs, xbs, yrs, ybs = w.strides(8)
+    strides = qfr.Strides(xrs, xbs, yrs, ybs)
+    ones = {}
+    for m in sorted(set(w.ms) | {1}):
+        y = run_mv(t, Wd, xd, n, k, m, batch, strides=strides)
+        yc = y.cpu().numpy()
+        ref, a = oracle_sampled(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows)
+        got = np.empty_like(ref)
+        for b in range(batch):
+            for j in range(m):
+                got[b, j] = yc[b * ybs + j * yrs + np.array(rows)]
+        ratio = check_tolerance(got, ref, a, f"{name} m={m}")
+        print(f"[workload] {name} m={m}: sampled {len(rows)} rows x {batch} batches ok, "
+              f"worst |err|/bound = {ratio:.3g}", flush=True)
+        ybits = bits(y)
+        if m == 1:
+            # m = 1 run of each input row j, for the row-exactness check
+            for j in range(8):
+                yj = run_mv(t, Wd, xd, n, k, 1, batch, strides=strides, x_offset=j * xrs)
+                ones[j] = bits(yj)
+        for j in range(m):
+            for b in range(batch):
+                o = b * ybs + j * yrs
+                assert np.array_equal(ybits[o:o + n], ones[j][b * ybs:b * ybs + n]), \
+                    f"{name}: m={m} row {j} batch {b} differs from m=1"
+        again = bits(run_mv(t, Wd, xd, n, k, m, batch, strides=strides))
+        assert np.array_equal(again, ybits), f"{name}: m={m} not repeatable"
