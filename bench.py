@@ -1,0 +1,317 @@
+"""Benchmark of the row-exact few-row mat-vec on one MI355X.
+
+A step is one pass of the hot path over the workload's m set: one
+row_exact_mv call per m (Q8_0 4096 x 4096 at m = 1, 4, 8 by default), each on
+the next of R copies of the weights so that the weights come from HBM rather
+than the 256 MB Infinity Cache (R copies >= 1 GiB).  Inputs are resident in
+HBM before timing.  The timed steps are replayed from a HIP graph captured on
+the bench stream (launch overhead off the clock); the step time is the wall
+time between two stream synchronisations around the replay.
+
+Prints one JSON line.  ``value`` is effective weight GB/s over the whole job
+(weight bytes of every call / wall time).  ``roofline`` is for the step's
+dominant kernel: algorithmic bytes per launch (weights + x + y) over its mean
+duration from HIP events on the bench stream.  ``cpu_baseline`` times the
+oracle (float64 CPU reference) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "effective weight GB/s and % of HBM peak, quantized GEMV at m=1/4/8"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="q8_0_4096x4096")
+    ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of weight copies to rotate through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle sample")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--sweep", default="", help="write per-(workload, m) kernel timings to this JSON file")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="launch the timed steps eagerly and exit (for rocprofv3 runs)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="only run a plain device copy of this many MiB, --steps times (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; traffic counters are reported only for the build they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_few_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, m):
+    """HBM bytes per launch of the (workload, m) kernel from the committed
+    rocprofv3 --pmc summary, or None when it is missing or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("launches", {}).get(f"{workload}:m{m}")
+    return None if ent is None else ent.get("hbm_bytes")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU; the mat-vec shards by weight rows with no "
+              "reduction, and multi-GPU runs are not part of it (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_few_row_amd as qfr
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        nbytes = int(args.copy_calibration * (1 << 20)) // 16 * 16
+        a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"bench.py: copied {nbytes} bytes {args.steps} times", flush=True)
+        return
+    w = wl.get(args.workload)
+    t, n, k, batch = w.wtype, w.n, w.k, w.batch
+    ms = list(w.ms) if args.workload != "q8_0_4096x4096" else [1, 4, 8]
+    xrs, xbs, yrs, ybs = w.strides(8)
+    strides = qfr.Strides(xrs, xbs, yrs, ybs)
+    wbytes = w.weight_bytes
+
+    W = w.make_weights()
+    x = w.make_x(8)
+    copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / wbytes)))
+    Wd = torch.empty((copies, wbytes), dtype=torch.uint8, device=dev)
+    src = torch.from_numpy(W.ravel()).to(dev)
+    for c in range(copies):
+        Wd[c].copy_(src)
+    del src
+    xd = torch.from_numpy(x.ravel().copy()).to(dev)
+    ybufs = {}
+    for m in ms:
+        _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, strides)
+        ybufs[m] = torch.zeros(yb // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    lib = qfr.load_library()
+
+    # Raw C-ABI calls (the binding's per-call Python checks are done once here).
+    import ctypes
+    sp = ctypes.byref(strides)
+    hs = stream.cuda_stream
+    wptrs = [Wd[c].data_ptr() for c in range(copies)]
+    xp = xd.data_ptr()
+    yptrs = {m: ybufs[m].data_ptr() for m in ms}
+    qfr.row_exact_mv(t, Wd[0], xd, ybufs[ms[0]], n, k, ms[0], batch, strides, stream=hs)  # checked path once
+
+    def launch(i, m):
+        rc = lib.row_exact_mv(int(t), wptrs[i % copies], xp, yptrs[m], n, k, m, batch, sp, hs)
+        if rc:
+            raise qfr.RowExactError(rc, qfr.row_exact_last_error())
+
+    def steps(first, count, events=None):
+        i = first
+        for s in range(count):
+            for m in ms:
+                if events is not None:
+                    events[m][0].append(torch.cuda.Event(enable_timing=True))
+                    events[m][1].append(torch.cuda.Event(enable_timing=True))
+                    events[m][0][-1].record(stream)
+                launch(i, m)
+                if events is not None:
+                    events[m][1][-1].record(stream)
+                i += 1
+        return i
+
+    with torch.cuda.stream(stream):
+        i = steps(0, args.warmup)
+    torch.cuda.synchronize()
+
+    if args.profile_only:
+        with torch.cuda.stream(stream):
+            steps(i, args.steps)
+        torch.cuda.synchronize()
+        print(f"bench.py: profile-only run of {args.steps} steps of {args.workload} done", flush=True)
+        return
+
+    # Per-kernel durations: HIP events around every launch of the timed steps,
+    # on the bench stream, eager.  A bounded spin kernel is queued first so
+    # that every launch and event is enqueued before the GPU reaches them:
+    # the kernels then run back to back and each event pair brackets one
+    # kernel, not the host's launch latency.
+    events = {m: ([], []) for m in ms}
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2e8))
+        steps(i, args.steps, events)
+    torch.cuda.synchronize()
+    kernel_us = {m: float(np.mean([a.elapsed_time(b) for a, b in zip(*events[m])]) * 1e3) for m in ms}
+
+    # Whole-job timing: graph replay of the same K steps (or eager with --eager).
+    y_eager = {m: ybufs[m].clone() for m in ms}
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            steps(i, args.steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        timing = "eager launches"
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            steps(i, args.steps)
+        torch.cuda.synchronize()
+        g.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        for m in ms:  # the graph recomputes the same outputs bit for bit
+            assert torch.equal(ybufs[m].view(torch.int32), y_eager[m].view(torch.int32)), "graph replay differs"
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        timing = "hip graph replay"
+
+    calls = args.steps * len(ms)
+    value = wbytes * calls / wall / 1e9
+    dom = max(ms, key=lambda m: kernel_us[m])
+    _, xb_dom, yb_dom = qfr.row_exact_required_bytes(t, n, k, dom, batch, strides)
+    alg_bytes = wbytes + xb_dom + yb_dom
+    achieved = alg_bytes / (kernel_us[dom] * 1e-6) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64 / Box-Muller blocks of the workload recipe)",
+        "config": {
+            "workload": args.workload, "weight_type": wl.TYPE_NAMES[t], "n": n, "k": k, "batch": batch,
+            "m": ms, "weight_bytes": wbytes, "cold_weight_copies": copies, "timing": timing,
+            "parallelism": "single GPU",
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "per_m": {str(m): {"kernel_us": round(kernel_us[m], 3),
+                           "weight_GBps": round(wbytes / (kernel_us[m] * 1e-6) / 1e9, 1),
+                           "hbm_frac": round(wbytes / (kernel_us[m] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                  for m in ms},
+        "kernel_source_hash": kernel_source_hash(),
+        "roofline": {
+            "kernel": f"mv_kernel<{wl.TYPE_NAMES[t]}, m={dom}>",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
+            "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_us": round(kernel_us[dom], 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, W, x, ms, args.cpu_seconds)
+    if args.sweep:
+        out["sweep_file"] = args.sweep
+        sweep(args.sweep, args.steps)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, W, x, ms, seconds):
+    """The oracle, single-threaded, on whole rows of the same workload: the
+    first S output rows at every m of the step, S chosen from a short probe so
+    the sample takes about ``seconds``."""
+    import oracle
+    t, n, k, batch = w.wtype, w.n, w.k, w.batch
+    xrs, xbs, _, _ = w.strides(8)
+    rb = oracle.row_bytes(t, k)
+    probe = max(1, min(n, 16))
+    t0 = time.perf_counter()
+    for m in ms:
+        oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, probe))
+    per_row = (time.perf_counter() - t0) / probe
+    rows = int(max(1, min(n, seconds / max(per_row, 1e-9))))
+    reps = max(1, int(seconds / max(per_row * rows, 1e-9)))  # whole steps, repeated up to ~seconds
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for m in ms:
+            oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, rows))
+    el = time.perf_counter() - t0
+    wbytes = rb * rows * batch * len(ms) * reps
+    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name}: first {rows} of {n} output rows x {batch} batch(es) at m={list(ms)}, "
+                      f"{reps} pass(es), float64 dequantize-then-dot, single thread, {el:.1f} s",
+            "seconds": round(el, 2)}
+
+
+def sweep(path, steps):
+    """Mean kernel time of every (workload, m) with cold weights, HIP events
+    around each eager launch."""
+    import numpy as np
+    import torch
+
+    import quantized_few_row_amd as qfr
+    import workloads as wl
+    res = []
+    for w in wl.WORKLOADS:
+        t, n, k, batch = w.wtype, w.n, w.k, w.batch
+        xrs, xbs, yrs, ybs = w.strides(8)
+        s = qfr.Strides(xrs, xbs, yrs, ybs)
+        W = w.make_weights()
+        copies = max(2, int(np.ceil((1 << 30) / w.weight_bytes)))
+        Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
+        xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        for m in sorted(set(w.ms) | {1, 4, 8}):
+            _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, s)
+            y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
+            for i in range(10):
+                qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
+            ev = []
+            for i in range(min(steps, 200)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
+                b.record()
+                ev.append((a, b))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in ev]) * 1e3)
+            sch = qfr.row_exact_schedule(t, n, k, m, batch)
+            res.append({"workload": w.name, "m": m, "kernel_us": round(us, 3),
+                        "weight_GBps": round(w.weight_bytes / us / 1e3, 1),
+                        "hbm_frac": round(w.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "schedule": sch.asdict()})
+            print(json.dumps(res[-1]), file=sys.stderr, flush=True)
+        del Wd
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,7 +92,7 @@ typedef struct {
  *  k_chunk              : packing.  Input values per row staged in LDS per
  *                         pass; >= k means one pass.  Otherwise a multiple of
  *                         the weight type's wave step (512 values for F16,
- *                         2048 for Q8_0 / Q4_K / Q5_0, 4096 for Q6_K).
+ *                         2048 for Q8_0 / Q5_0, 4096 for Q4_K / Q6_K).
  * Packing fields never change the bits of y. */
 typedef struct {
     uint32_t k_split;

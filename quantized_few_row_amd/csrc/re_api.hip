@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -193,15 +194,55 @@ int validate_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint
 // 64-lane tree sum of one wave's lane chains.
 uint32_t derived_k_split(int, uint32_t) { return 1; }
 
+MvAttributes mv_attributes(int t) {
+    switch (t) {
+    case kF16: return attributes_mv_f16;
+    case kQ8_0: return attributes_mv_q8_0;
+    case kQ4K: return attributes_mv_q4_k;
+    case kQ6K: return attributes_mv_q6_k;
+    default: return attributes_mv_q5_0;
+    }
+}
+
+// Workgroups of a kernel instance that fit on one CU at once: VGPRs (512 per
+// SIMD lane, 4 SIMDs, waves of a workgroup spread over the SIMDs), at most 8
+// waves per SIMD, and LDS.
+int workgroups_per_cu(int t, uint32_t m, uint32_t nr, uint32_t waves, size_t lds, size_t lds_per_cu) {
+    hipFuncAttributes attr;
+    if (mv_attributes(t)(m, nr, &attr) != hipSuccess) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    const int vg = attr.numRegs > 0 ? (attr.numRegs + 7) / 8 * 8 : 256;
+    int per_simd = 512 / vg;
+    if (per_simd > 8) per_simd = 8;
+    const int waves_per_simd_per_wg = (int)((waves + 3) / 4);
+    int by_regs = per_simd / waves_per_simd_per_wg;
+    int by_lds = lds ? (int)(lds_per_cu / lds) : 8;
+    int r = by_regs < by_lds ? by_regs : by_lds;
+    if (r > 8) r = 8;
+    if (getenv("ROW_EXACT_DEBUG"))
+        fprintf(stderr, "row_exact_mv: kernel %s m=%u rows/wave=%u: %d VGPRs, %d waves/SIMD, lds %zu -> %d workgroups/CU\n",
+                type_name(t), m, nr, attr.numRegs, per_simd, lds, r < 1 ? 1 : r);
+    return r < 1 ? 1 : r;
+}
+
+// Most rows per wave whose kernel holds all its state in registers at this m.
+uint32_t max_rows_per_wave(int t, uint32_t m) {
+    if ((t == kQ4K || t == kQ6K) && m >= 5) return 2;
+    return 4;
+}
+
 int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, row_exact_schedule_t &s) {
     DevInfo di;
     int rc = device_info(di);
     if (rc) return rc;
     s.k_split = derived_k_split(t, k);
-    // rows per wave: the most that still leaves >= 8 waves per CU
+    // rows per wave: the most that still leaves enough waves (16 per CU for
+    // m <= 2, where the loads dominate; 8 above)
     const uint64_t rows = (uint64_t)n * batch;
-    const uint64_t target_waves = (uint64_t)di.cus * 8;
-    uint32_t nr = 4;
+    const uint64_t target_waves = (uint64_t)di.cus * (m <= 2 ? 16 : 8);
+    uint32_t nr = max_rows_per_wave(t, m);
     while (nr > 1 && rows / nr < target_waves) nr >>= 1;
     s.rows_per_wave = nr;
     const uint32_t gpb = (n + nr - 1) / nr;
@@ -216,15 +257,14 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         while (kc + step < k && lds_bytes(t, m, k, kc + step) <= di.lds_max) kc += step;
     }
     s.k_chunk = kc;
-    // workgroups: single pass -> persistent-ish, up to 2 per CU; several passes -> one row group per wave
+    // workgroups: single pass -> as many as fit on the device at once (each
+    // then walks its share of row groups); several passes -> one row group
+    // per wave
     const uint32_t max_wgs = (gpb + waves - 1) / waves;
     uint32_t wgs;
     if (kc >= k) {
-        const size_t l = lds_bytes(t, m, k, kc);
-        uint64_t per_cu = l ? di.lds_max / l : 2;
-        if (per_cu < 1) per_cu = 1;
-        if (per_cu > 2) per_cu = 2;
-        const uint64_t target = (uint64_t)di.cus * per_cu;
+        const int per_cu = workgroups_per_cu(t, m, nr, waves, lds_bytes(t, m, k, kc), di.lds_max);
+        const uint64_t target = (uint64_t)di.cus * (uint64_t)per_cu;
         uint64_t w = (target + batch - 1) / batch;
         if (w < 1) w = 1;
         wgs = (uint32_t)(w < max_wgs ? w : max_wgs);

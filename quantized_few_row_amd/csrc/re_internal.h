@@ -44,9 +44,9 @@ template <> struct Geo<kQ8_0> {  // piece: one 34-byte block
     static constexpr int PV = 32, NG = 8, PADP = 32;
     __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 32; }
 };
-template <> struct Geo<kQ4K> {   // piece: 16 nibble bytes of a super-block (32 values)
-    static constexpr int PV = 32, NG = 8, PADP = 64;
-    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 256 * 8; }
+template <> struct Geo<kQ4K> {   // piece: one 32-byte nibble chunk of a super-block (64 values)
+    static constexpr int PV = 64, NG = 16, PADP = 64;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 256 * 4; }
 };
 template <> struct Geo<kQ6K> {   // piece: a quarter super-block (64 values)
     static constexpr int PV = 64, NG = 16, PADP = 128;
@@ -90,12 +90,18 @@ inline uint32_t pad_period(int t) {
 typedef hipError_t (*MvLauncher)(const MvArgs &, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds,
                                  hipStream_t s);
 typedef hipError_t (*DqLauncher)(const DqArgs &, hipStream_t s);
+typedef hipError_t (*MvAttributes)(uint32_t m, uint32_t nr, hipFuncAttributes *attr);
 
 hipError_t launch_mv_f16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t launch_mv_q8_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t launch_mv_q4_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t launch_mv_q6_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t launch_mv_q5_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t attributes_mv_f16(uint32_t, uint32_t, hipFuncAttributes *);
+hipError_t attributes_mv_q8_0(uint32_t, uint32_t, hipFuncAttributes *);
+hipError_t attributes_mv_q4_k(uint32_t, uint32_t, hipFuncAttributes *);
+hipError_t attributes_mv_q6_k(uint32_t, uint32_t, hipFuncAttributes *);
+hipError_t attributes_mv_q5_0(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t launch_dq_f16(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q8_0(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q4_k(const DqArgs &, hipStream_t);

@@ -47,6 +47,13 @@ __device__ __forceinline__ float h2f(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// Hides a value from the optimizer so that byte-parallel (SWAR) code stays
+// byte-parallel instead of being folded back into per-value bit extracts.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // ({hi, lo} >> 8*sh)[31:0]
 __device__ __forceinline__ uint32_t abyte(uint32_t hi, uint32_t lo, uint32_t sh) {
     return __builtin_amdgcn_alignbyte(hi, lo, sh);
@@ -151,9 +158,12 @@ template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
 // Piece p: block p (22 bytes: f16 d, u32 high bits, 16 nibble bytes).
 // Value i < 16: low nibble of byte i; i >= 16: high nibble of byte i - 16;
 // bit i of the high bits is bit 4.  w = d * (q - 16).
+// Four values at a time: byte i of a dword becomes the int8 8*(q_i - 16)
+// (nibble in bits 3..6, inverted high bit as the sign bit), converted with
+// one signed-byte convert and scaled by d/8 (exact).
 template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
-    struct Raw { uint32_t qs[4]; uint32_t qh; uint32_t d; };
-    struct Pre { float d; };
+    struct Raw { uint32_t qs[4]; uint32_t nqh; uint32_t d; };
+    struct Pre { float d8; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
         const uint32_t B = o0 + 22 * p;
@@ -162,20 +172,18 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
         const uint32_t b0 = abyte(e.y, e.x, sh);     // d | qh.lo << 16
         const uint32_t b1 = abyte(e.z, e.y, sh);     // qh.hi | qs[0..1] << 16
         r.d = b0 & 0xffffu;
-        r.qh = abyte(b1, b0, 2);
+        r.nqh = ~abyte(b1, b0, 2);
         load16_a2(R, B + 6, r.qs);
         return r;
     }
-    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d)}; }
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d) * 0.125f}; }
     static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
-        const uint32_t dw = r.qs[g & 3];
-        const int nsh = g >= 4 ? 4 : 0;
+        const uint32_t lo = g < 4 ? ((r.qs[g] << 3) & 0x78787878u) : ((r.qs[g & 3] >> 1) & 0x78787878u);
+        // bits 4g..4g+3 of ~qh -> bit 7 of bytes 0..3 (t * 0x204081 puts bit i at 8i, no carries)
+        const uint32_t t = (r.nqh >> (4 * g)) & 15u;
+        const uint32_t b = ((opaque(__umul24(t, 0x204081u)) << 7) & 0x80808080u) | lo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = (dw >> (8 * i + nsh)) & 15u;
-            const uint32_t hb = (r.qh >> (4 * g + i)) & 1u;
-            w[i] = pr.d * (float)((int)(lo | (hb << 4)) - 16);
-        }
+        for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.d8;
     }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 32 * p + 4 * g; }
     static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) { return 36 * (p - vb / 32); }
@@ -184,65 +192,59 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
 };
 
 // ---------------------------------------------------------------- Q4_K
-// Piece p: super-block p/8, nibble bytes 16q..16q+15 (q = p % 8) of its 128;
-// they hold chunk c = q/2: low nibbles are values 64c + 16(q%2) + 0..15 of
-// sub-block 2c, high nibbles values 64c + 32 + 16(q%2) + 0..15 of sub-block
-// 2c+1.  w = fma(d*sc, q, -(dmin*mn)): one rounding of the exact value.
+// Piece p: super-block p/4, nibble chunk c = p%4 (bytes 32c..32c+31 of its
+// 128): low nibbles are values 64c + 0..31 of sub-block 2c, high nibbles
+// values 64c + 32..63 of sub-block 2c+1.
+// w = fma(d*sc, q, -(dmin*mn)): one rounding of the exact value.
 template <> struct Tr<kQ4K> : Geo<kQ4K> {
-    struct Raw { uint32_t qs[4]; uint32_t h[4]; };
+    struct Raw { uint32_t qs[8]; uint32_t h[4]; };
     struct Pre { float dsc[2], dmn[2]; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
-        const uint32_t B = o0 + 144 * (p >> 3);
+        const uint32_t B = o0 + 144 * (p >> 2);
         const u32x4 hv = ldv<u32x4>(R, B);
-        const u32x4 qv = ldv<u32x4>(R, B + 16 + 16 * (p & 7));
+        const u32x4 q0 = ldv<u32x4>(R, B + 16 + 32 * (p & 3));
+        const u32x4 q1 = ldv<u32x4>(R, B + 32 + 32 * (p & 3));
         r.h[0] = hv.x; r.h[1] = hv.y; r.h[2] = hv.z; r.h[3] = hv.w;
-        r.qs[0] = qv.x; r.qs[1] = qv.y; r.qs[2] = qv.z; r.qs[3] = qv.w;
+        r.qs[0] = q0.x; r.qs[1] = q0.y; r.qs[2] = q0.z; r.qs[3] = q0.w;
+        r.qs[4] = q1.x; r.qs[5] = q1.y; r.qs[6] = q1.z; r.qs[7] = q1.w;
         return r;
     }
-    // 6-bit scale and min of sub-block s from the 12 packed bytes
-    // (h[1] = bytes 0..3, h[2] = bytes 4..7, h[3] = bytes 8..11).
-    static __device__ __forceinline__ void scale_min(const uint32_t (&h)[4], uint32_t s, uint32_t &sc,
-                                                     uint32_t &mn) {
-        if (s < 4) {
-            sc = (h[1] >> (8 * s)) & 63u;
-            mn = (h[2] >> (8 * s)) & 63u;
-        } else {
-            const uint32_t u = 8 * (s - 4);
-            sc = ((h[3] >> u) & 15u) | (((h[1] >> (u + 6)) & 3u) << 4);
-            mn = ((h[3] >> (u + 4)) & 15u) | (((h[2] >> (u + 6)) & 3u) << 4);
-        }
-    }
+    // Scales and mins of sub-blocks 2c and 2c+1 as byte pairs.  With the 12
+    // packed bytes S in h[1] (S0..3), h[2] (S4..7), h[3] (S8..11):
+    //   s < 4 : sc = S[s] & 63,                     mn = S[s+4] & 63
+    //   s >= 4: sc = (S[s+4] & 15) | (S[s-4] >> 6) << 4,
+    //           mn = (S[s+4] >> 4) | (S[s] >> 6) << 4
     static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t p) {
         Pre pr;
+        const uint32_t c = p & 3;
+        const bool hi = c >= 2;
+        const uint32_t sh = 16 * (c & 1);
+        const uint32_t top = sh + (hi ? 2u : 0u);
+        const uint32_t scp = (((hi ? r.h[3] : r.h[1]) >> sh) & 0x0F0Fu) | ((r.h[1] >> top) & 0x3030u);
+        const uint32_t mnp = (((hi ? r.h[3] : r.h[2]) >> (sh + (hi ? 4u : 0u))) & 0x0F0Fu) | ((r.h[2] >> top) & 0x3030u);
         const float d = h2f(r.h[0] & 0xffffu), dmin = h2f(r.h[0] >> 16);
-        const uint32_t s0 = ((p & 7) >> 1) * 2;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            uint32_t sc, mn;
-            scale_min(r.h, s0 + e, sc, mn);
-            pr.dsc[e] = d * (float)sc;     // exact
-            pr.dmn[e] = dmin * (float)mn;  // exact
-        }
+        pr.dsc[0] = d * (float)(scp & 0xffu);       // exact
+        pr.dsc[1] = d * (float)(scp >> 8);
+        pr.dmn[0] = dmin * (float)(mnp & 0xffu);
+        pr.dmn[1] = dmin * (float)(mnp >> 8);
         return pr;
     }
     static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
-        const int e = g >= 4 ? 1 : 0;
-        const uint32_t dw = r.qs[g & 3];
+        const int e = g >= 8 ? 1 : 0;
+        const uint32_t dw = r.qs[g & 7];
+        const uint32_t q4 = opaque(e ? ((dw >> 4) & 0x0F0F0F0Fu) : (dw & 0x0F0F0F0Fu));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w[i] = __builtin_fmaf(pr.dsc[e], (float)((dw >> (8 * i + 4 * e)) & 15u), -pr.dmn[e]);
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(pr.dsc[e], (float)((q4 >> (8 * i)) & 0xffu), -pr.dmn[e]);
     }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) {
-        const uint32_t q = p & 7;
-        return 256 * (p >> 3) + 64 * (q >> 1) + 16 * (q & 1) + (g >= 4 ? 32 : 0) + 4 * (g & 3);
+        return 256 * (p >> 2) + 64 * (p & 3) + (g >= 8 ? 32 : 0) + 4 * (g & 7);
     }
     // PADP 64: pad index = 4*(super-block) + chunk
     static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
-        const uint32_t sb = (p >> 3) - vb / 256, q = p & 7;
-        return 272 * sb + 68 * (q >> 1) + 16 * (q & 1);
+        return 272 * ((p >> 2) - vb / 256) + 68 * (p & 3);
     }
-    static constexpr uint32_t goff(int g) { return (g >= 4 ? 32 : 0) + 4 * (g & 3); }
+    static constexpr uint32_t goff(int g) { return (g >= 8 ? 32 : 0) + 4 * (g & 7); }
     static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
 };
 
@@ -253,15 +255,17 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
 // from bits 2t..2t+1 of qh[32hh + l], scale sc[8hh + 2t + l0/16].
 // w = (d * sc) * (q - 32), exact.
 template <> struct Tr<kQ6K> : Geo<kQ6K> {
-    struct Raw { uint32_t ql0[4], ql1[4], qh[4], sc[2], d; };
-    struct Pre { float ds[4]; };
+    struct Raw { uint32_t ql0[4], ql1[4], qhx[4], sc[2], d; };
+    struct Pre { float ds4[4]; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
         const uint32_t hh = (p >> 1) & 1, l0 = 16 * (p & 1);
         const uint32_t B = o0 + 210 * (p >> 2);
         load16_a2(R, B + 64 * hh + l0, r.ql0);
         load16_a2(R, B + 64 * hh + 32 + l0, r.ql1);
-        load16_a2(R, B + 128 + 32 * hh + l0, r.qh);
+        load16_a2(R, B + 128 + 32 * hh + l0, r.qhx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.qhx[i] ^= 0xAAAAAAAAu;  // invert bit 1 of every 2-bit high part
         const uint32_t G = B + 192 + 8 * hh;  // sc[8hh .. 8hh+7]
         const uint32_t sh = G & 3u;
         const u32x2a4 v = ldv<u32x2a4>(R, G - sh);
@@ -278,21 +282,22 @@ template <> struct Tr<kQ6K> : Geo<kQ6K> {
         for (int t = 0; t < 4; ++t) {
             const uint32_t idx = 2 * t + (p & 1);
             const int8_t s = (int8_t)(r.sc[idx >> 2] >> (8 * (idx & 3)));
-            pr.ds[t] = d * (float)s;  // exact
+            pr.ds4[t] = d * (float)s * 0.25f;  // exact: d*sc, then a power of two
         }
         return pr;
     }
+    // Four values at a time: byte i becomes the int8 4*(q_i - 32) (low 4
+    // bits in bits 2..5, high 2 bits in bits 6..7 with the top one inverted,
+    // the inversion applied to qh at load), converted with one signed-byte
+    // convert and scaled by d*sc/4: exactly d*sc*(q-32), sign of zero
+    // included.
     static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
         const int t = g >> 2, G = g & 3;
-        const uint32_t ldw = (t & 1) ? r.ql1[G] : r.ql0[G];
-        const int nsh = t >= 2 ? 4 : 0;
-        const uint32_t hdw = r.qh[G];
+        const uint32_t src = (t & 1) ? r.ql1[G] : r.ql0[G];
+        const uint32_t lo = t < 2 ? ((src << 2) & 0x3C3C3C3Cu) : ((src >> 2) & 0x3C3C3C3Cu);
+        const uint32_t b = ((r.qhx[G] << (6 - 2 * t)) & 0xC0C0C0C0u) | lo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = (ldw >> (8 * i + nsh)) & 15u;
-            const uint32_t hi = (hdw >> (8 * i + 2 * t)) & 3u;
-            w[i] = pr.ds[t] * (float)((int)(lo | (hi << 4)) - 32);
-        }
+        for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.ds4[t];
     }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) {
         return 256 * (p >> 2) + 128 * ((p >> 1) & 1) + 32 * (g >> 2) + 16 * (p & 1) + 4 * (g & 3);
@@ -395,14 +400,29 @@ __device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *_
 template <int T, int M>
 __device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
                                         uint32_t v0, uint32_t v1, uint32_t XS) {
+    // Up to 8 float4 loads per thread in flight before the LDS writes.
+    constexpr int U = M >= 8 ? 1 : 8 / M;
     const uint32_t n4 = (v1 - v0) >> 2;
+    const uint32_t nt = blockDim.x;
+    for (uint32_t q0 = threadIdx.x; q0 < n4; q0 += U * nt) {
+        f32x4 v[U][M];
 #pragma unroll
-    for (int j = 0; j < M; ++j) {
-        const float *src = xb + (uint64_t)j * xrs + v0;
-        float *dst = xs + j * XS;
-        for (uint32_t q = threadIdx.x; q < n4; q += blockDim.x) {
-            const uint32_t lv = q << 2;
-            *(f32x4 *)(dst + lv + 4 * (lv / Geo<T>::PADP)) = *(const f32x4 *)(src + lv);
+        for (int u = 0; u < U; ++u) {
+            const uint32_t q = q0 + u * nt;
+            if (q < n4) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) v[u][j] = *(const f32x4 *)(xb + (uint64_t)j * xrs + v0 + 4 * q);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t q = q0 + u * nt;
+            if (q < n4) {
+                const uint32_t lv = 4 * q;
+                const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+#pragma unroll
+                for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = v[u][j];
+            }
         }
     }
 }
@@ -480,6 +500,61 @@ __device__ __forceinline__ void row_bases(const uint8_t *Wb, uint64_t row_bytes,
     }
 }
 
+template <int T, int NR>
+__device__ __forceinline__ void load_item(const uint8_t *Wb, const MvArgs &a, uint32_t g, uint32_t p,
+                                          typename Tr<T>::Raw (&raw)[NR]) {
+    const uint8_t *R[NR];
+    uint32_t o0[NR];
+    row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) raw[r] = Tr<T>::load(R[r], o0[r], p, a.k);
+}
+
+template <int M, int NR> __device__ __forceinline__ void zero(float (&acc)[NR][M]) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int j = 0; j < M; ++j) acc[r][j] = 0.0f;
+}
+
+// Items in flight ahead of the one being multiplied (1 or 2), chosen so the
+// raw buffers of 1 + DEPTH items stay within the register budget.
+template <int T, int M, int NR> struct Depth {
+    static constexpr int raw_dwords = (int)(sizeof(typename Tr<T>::Raw) / 4) * NR;
+    static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= 120) ? 2 : 1;
+};
+
+// One step of the single-pass walk.  Items are (row group g, wave step s):
+// pieces 64s + lane of the group's NR rows.  The load cursor (lg, ls) runs
+// DEPTH items ahead of the compute cursor (cg, cs): the step loads the item
+// at the load cursor into `nxt`, multiplies `cur`, and stores a group's
+// outputs after its last step.  Returns whether items remain.
+template <int T, int M, int NR>
+__device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__restrict__ Wb, float *__restrict__ yb,
+                                          const float *__restrict__ xs, uint32_t XS, uint32_t &lg, uint32_t &ls,
+                                          uint32_t &cg, uint32_t &cs, uint32_t gstride, uint32_t g1, uint32_t S,
+                                          uint32_t lane, const typename Tr<T>::Raw (&cur)[NR],
+                                          typename Tr<T>::Raw (&nxt)[NR], float (&acc)[NR][M]) {
+    if (lg < g1) {
+        load_item<T, NR>(Wb, a, lg, min(ls * 64 + lane, a.pieces - 1), nxt);
+        if (++ls == S) {
+            ls = 0;
+            lg += gstride;
+        }
+    }
+    const uint32_t pc = cs * 64 + lane;
+    if (pc < a.pieces) compute_piece<T, M, NR>(acc, cur, pc, 0, xs, XS, a.k);
+    if (cs == S - 1) {
+        reduce_store<M, NR>(acc, yb, a.yrs, a.n, cg * NR, lane);
+        zero<M, NR>(acc);
+    }
+    if (++cs == S) {
+        cs = 0;
+        cg += gstride;
+    }
+    return cg < g1;
+}
+
 // ---------------------------------------------------------------- kernels
 
 template <int T, int M, int NR>
@@ -499,29 +574,54 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     const uint32_t XS = a.xs_stride;
 
     if (a.nchunks == 1) {
+        // Single pass: the wave walks (row group, wave step) items of its
+        // groups g0+wave, g0+wave+nwaves, ... with DEPTH items of loads in
+        // flight.  The first DEPTH items are requested before x is staged.
+        using Raw = typename Tr<T>::Raw;
+        constexpr int DEPTH = Depth<T, M, NR>::value;
+        const uint32_t S = (a.pieces + 63) >> 6;
+        uint32_t lg = g0 + wave, ls = 0;
+        const uint32_t gfirst = lg;
+        Raw A[NR], B[NR], C[NR];
+        if (lg < g1) {
+            load_item<T, NR>(Wb, a, lg, min(lane, a.pieces - 1), A);
+            if (++ls == S) {
+                ls = 0;
+                lg += nwaves;
+            }
+        }
+        if (DEPTH == 2 && lg < g1) {
+            load_item<T, NR>(Wb, a, lg, min(ls * 64 + lane, a.pieces - 1), B);
+            if (++ls == S) {
+                ls = 0;
+                lg += nwaves;
+            }
+        }
         stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
         __syncthreads();
-        for (uint32_t g = g0 + wave; g < g1; g += nwaves) {
+        if (gfirst < g1) {
             float acc[NR][M];
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-#pragma unroll
-                for (int j = 0; j < M; ++j) acc[r][j] = 0.0f;
-            const uint8_t *R[NR];
-            uint32_t o0[NR];
-            row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
-            accumulate<T, M, NR>(acc, R, o0, 0, a.pieces, 0, xs, XS, a.k, lane);
-            reduce_store<M, NR>(acc, yb, a.yrs, a.n, g * NR, lane);
+            zero<M, NR>(acc);
+            uint32_t cg = gfirst, cs = 0;
+            if constexpr (DEPTH == 2) {
+                while (walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, A, C, acc) &&
+                       walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, B, A, acc) &&
+                       walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, C, B, acc)) {
+                }
+            } else {
+                while (walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, A, B, acc) &&
+                       walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, B, A, acc)) {
+                }
+            }
         }
     } else {
+        // Several LDS passes over K: every wave of the workgroup works on one
+        // row group per round and all waves stage each pass together.
         for (uint32_t base = g0; base < g1; base += nwaves) {
             const uint32_t g = base + wave;
             const bool active = g < g1;
             float acc[NR][M];
-#pragma unroll
-            for (int r = 0; r < NR; ++r)
-#pragma unroll
-                for (int j = 0; j < M; ++j) acc[r][j] = 0.0f;
+            zero<M, NR>(acc);
             const uint8_t *R[NR];
             uint32_t o0[NR];
             row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
@@ -575,6 +675,36 @@ hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStr
     MvArgs copy = a;
     void *args[] = {&copy};
     return hipLaunchKernel(fn, grid, block, args, lds, s);
+}
+
+template <int T, int M, int NR>
+hipError_t attributes_one(hipFuncAttributes *attr) {
+    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR>);
+}
+
+template <int T, int M>
+hipError_t attributes_m(uint32_t nr, hipFuncAttributes *attr) {
+    switch (nr) {
+    case 1: return attributes_one<T, M, 1>(attr);
+    case 2: return attributes_one<T, M, 2>(attr);
+    case 4: return attributes_one<T, M, 4>(attr);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+hipError_t attributes_mv(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {
+    switch (m) {
+    case 1: return attributes_m<T, 1>(nr, attr);
+    case 2: return attributes_m<T, 2>(nr, attr);
+    case 3: return attributes_m<T, 3>(nr, attr);
+    case 4: return attributes_m<T, 4>(nr, attr);
+    case 5: return attributes_m<T, 5>(nr, attr);
+    case 6: return attributes_m<T, 6>(nr, attr);
+    case 7: return attributes_m<T, 7>(nr, attr);
+    case 8: return attributes_m<T, 8>(nr, attr);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int T, int M>

@@ -8,6 +8,10 @@ hipError_t launch_mv_f16(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, di
     return launch_mv<kF16>(a, m, nr, grid, block, lds, s);
 }
 
+hipError_t attributes_mv_f16(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {
+    return attributes_mv<kF16>(m, nr, attr);
+}
+
 hipError_t launch_dq_f16(const DqArgs &a, hipStream_t s) { return launch_dq<kF16>(a, s); }
 
 }  // namespace rex

@@ -8,6 +8,10 @@ hipError_t launch_mv_q4_k(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, d
     return launch_mv<kQ4K>(a, m, nr, grid, block, lds, s);
 }
 
+hipError_t attributes_mv_q4_k(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {
+    return attributes_mv<kQ4K>(m, nr, attr);
+}
+
 hipError_t launch_dq_q4_k(const DqArgs &a, hipStream_t s) { return launch_dq<kQ4K>(a, s); }
 
 }  // namespace rex

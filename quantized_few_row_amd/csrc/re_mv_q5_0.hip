@@ -8,6 +8,10 @@ hipError_t launch_mv_q5_0(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, d
     return launch_mv<kQ5_0>(a, m, nr, grid, block, lds, s);
 }
 
+hipError_t attributes_mv_q5_0(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {
+    return attributes_mv<kQ5_0>(m, nr, attr);
+}
+
 hipError_t launch_dq_q5_0(const DqArgs &a, hipStream_t s) { return launch_dq<kQ5_0>(a, s); }
 
 }  // namespace rex

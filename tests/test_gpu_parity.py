@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = {
     wl.F16: (77, 1028),    # 129 pieces of 8 values, the last one half
     wl.Q8_0: (70, 2080),   # 65 blocks
-    wl.Q4_K: (67, 2304),   # 9 super-blocks = 72 pieces
+    wl.Q4_K: (67, 4352),   # 17 super-blocks = 68 pieces
     wl.Q6_K: (41, 4352),   # 17 super-blocks = 68 pieces
     wl.Q5_0: (53, 2112),   # 66 blocks
 }
@@ -82,7 +82,7 @@ def test_repeat_bitwise(t, data):
 
 
 def _schedules(t, k):
-    step = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 2048, wl.Q6_K: 4096, wl.Q5_0: 2048}[t]
+    step = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048}[t]
     out = []
     for nr in (1, 2, 4):
         for waves, wgs in ((1, 1), (1, 1000), (4, 3), (8, 2), (8, 64), (3, 5)):
