@@ -238,10 +238,35 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     int rc = device_info(di);
     if (rc) return rc;
     s.k_split = derived_k_split(t, k);
-    // rows per wave: the most that still leaves enough waves (16 per CU for
-    // m <= 2, where the loads dominate; 8 above)
     const uint64_t rows = (uint64_t)n * batch;
-    const uint64_t target_waves = (uint64_t)di.cus * (m <= 2 ? 16 : 8);
+    const uint32_t step = wave_step_values(t);
+    // LDS passes: one if the m staged rows fit, else the largest wave-step multiple that fits
+    uint32_t kc = k;
+    if (lds_bytes(t, m, k, k) > di.lds_max) {
+        kc = step;
+        while (kc + step < k && lds_bytes(t, m, k, kc + step) <= di.lds_max) kc += step;
+    }
+    s.k_chunk = kc;
+    if (m <= 2 && kc >= k) {
+        // Few input rows: the weight loads dominate.  Measured best on
+        // MI355X: about 32 waves per CU over the whole grid (the hardware
+        // balances the tail across workgroups), one row group per wave while
+        // the rows allow it, single rows beyond that.
+        const uint64_t target = (uint64_t)di.cus * 32;
+        const uint32_t nr = (rows > target && rows <= 2 * target) ? 2u : 1u;
+        s.rows_per_wave = nr;
+        const uint32_t gpb = (n + nr - 1) / nr;
+        uint32_t waves = 8;
+        while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
+        s.waves_per_workgroup = waves;
+        const uint32_t max_wgs = (gpb + waves - 1) / waves;
+        uint64_t w = (target / waves + batch - 1) / batch;
+        if (w < 1) w = 1;
+        s.workgroups_per_batch = (uint32_t)(w < max_wgs ? w : max_wgs);
+        return 0;
+    }
+    // rows per wave: the most that still leaves 8 waves per CU
+    const uint64_t target_waves = (uint64_t)di.cus * 8;
     uint32_t nr = max_rows_per_wave(t, m);
     while (nr > 1 && rows / nr < target_waves) nr >>= 1;
     s.rows_per_wave = nr;
@@ -249,14 +274,6 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     uint32_t waves = 8;
     while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
     s.waves_per_workgroup = waves;
-    // LDS passes: one if the m staged rows fit, else the largest wave-step multiple that fits
-    const uint32_t step = wave_step_values(t);
-    uint32_t kc = k;
-    if (lds_bytes(t, m, k, k) > di.lds_max) {
-        kc = step;
-        while (kc + step < k && lds_bytes(t, m, k, kc + step) <= di.lds_max) kc += step;
-    }
-    s.k_chunk = kc;
     // workgroups: single pass -> as many as fit on the device at once (each
     // then walks its share of row groups); several passes -> one row group
     // per wave

@@ -15,12 +15,17 @@
 //     (padded so that the lanes' 16-byte reads hit distinct banks).
 //
 // Numerics (module docs, "Row exactness")
-//   - Every weight is decoded to its exact float32 value in registers (Q4_K's
-//     value is one rounding of an exact difference, via fma).
+//   - Every weight is decoded exactly in registers.  F16 and Q4_K weights are
+//     decoded to their float32 value w (Q4_K's is one rounding of an exact
+//     difference, via fma).  Q8_0, Q5_0 and Q6_K weights are s * q with an
+//     integer-valued q and a scale s shared by a segment of values (a block;
+//     16 values for Q6_K): they are decoded to q, exactly.
 //   - For each (row, input row) a lane keeps one accumulator and folds its
-//     pieces' products into it with an explicit fmaf chain, in piece order
-//     and, inside a piece, in a fixed value order.  Nothing about that chain
-//     depends on m or on the packing (NR, waves per workgroup, grid).
+//     pieces into it with an explicit fmaf chain, in piece order and, inside
+//     a piece, in a fixed value order: acc = fma(w, x, acc) per value, or,
+//     per scaled segment, part = q*x then fma(q, x, part) over its values and
+//     acc = fma(s, part, acc).  Nothing about those chains depends on m or on
+//     the packing (NR, waves per workgroup, grid).
 //   - The 64 lane partials of an output are added by one fixed tree: lanes
 //     (L, L^32), then (L, L^16), then within each row of 16 lanes: rotate-8,
 //     half-row mirror, xor 2, xor 1.  The first two levels are done with the
@@ -93,6 +98,7 @@ template <int T> struct Tr;
 // ---------------------------------------------------------------- F16
 // Piece p: values 8p..8p+7 (16 bytes).  k % 8 == 4 leaves a half piece.
 template <> struct Tr<kF16> : Geo<kF16> {
+    static constexpr int SEG = 0;  // no scale: the fma chain runs on w
     struct Raw { uint32_t w[4]; };
     struct Pre {};
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t k) {
@@ -128,6 +134,7 @@ template <> struct Tr<kF16> : Geo<kF16> {
 // ---------------------------------------------------------------- Q8_0
 // Piece p: block p (34 bytes: f16 d, 32 int8).  w = d * q.
 template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
+    static constexpr int SEG = 8;  // one scale per piece
     struct Raw { uint32_t q[8]; uint32_t d; };
     struct Pre { float d; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -148,6 +155,11 @@ template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pr.d * (float)(int8_t)(r.q[g] >> (8 * i));
     }
+    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(r.q[g] >> (8 * i));
+    }
+    static __device__ __forceinline__ float scale(const Pre &pr, int) { return pr.d; }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 32 * p + 4 * g; }
     static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) { return 36 * (p - vb / 32); }
     static constexpr uint32_t goff(int g) { return 4 * g; }
@@ -162,6 +174,7 @@ template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
 // (nibble in bits 3..6, inverted high bit as the sign bit), converted with
 // one signed-byte convert and scaled by d/8 (exact).
 template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
+    static constexpr int SEG = 8;  // one scale per piece
     struct Raw { uint32_t qs[4]; uint32_t nqh; uint32_t d; };
     struct Pre { float d8; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -177,14 +190,23 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
         return r;
     }
     static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d) * 0.125f}; }
-    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+    static __device__ __forceinline__ uint32_t bytes8(const Raw &r, int g) {
         const uint32_t lo = g < 4 ? ((r.qs[g] << 3) & 0x78787878u) : ((r.qs[g & 3] >> 1) & 0x78787878u);
         // bits 4g..4g+3 of ~qh -> bit 7 of bytes 0..3 (t * 0x204081 puts bit i at 8i, no carries)
         const uint32_t t = (r.nqh >> (4 * g)) & 15u;
-        const uint32_t b = ((opaque(__umul24(t, 0x204081u)) << 7) & 0x80808080u) | lo;
+        return ((opaque(__umul24(t, 0x204081u)) << 7) & 0x80808080u) | lo;
+    }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+        const uint32_t b = bytes8(r, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.d8;
     }
+    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+        const uint32_t b = bytes8(r, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(b >> (8 * i));
+    }
+    static __device__ __forceinline__ float scale(const Pre &pr, int) { return pr.d8; }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 32 * p + 4 * g; }
     static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) { return 36 * (p - vb / 32); }
     static constexpr uint32_t goff(int g) { return 4 * g; }
@@ -197,6 +219,7 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
 // values 64c + 32..63 of sub-block 2c+1.
 // w = fma(d*sc, q, -(dmin*mn)): one rounding of the exact value.
 template <> struct Tr<kQ4K> : Geo<kQ4K> {
+    static constexpr int SEG = 0;  // w = d*sc*q - dmin*mn is formed per value (the offset does not factor)
     struct Raw { uint32_t qs[8]; uint32_t h[4]; };
     struct Pre { float dsc[2], dmn[2]; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -255,6 +278,7 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
 // from bits 2t..2t+1 of qh[32hh + l], scale sc[8hh + 2t + l0/16].
 // w = (d * sc) * (q - 32), exact.
 template <> struct Tr<kQ6K> : Geo<kQ6K> {
+    static constexpr int SEG = 4;  // one scale per 16 values (groups 4t..4t+3)
     struct Raw { uint32_t ql0[4], ql1[4], qhx[4], sc[2], d; };
     struct Pre { float ds4[4]; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -291,14 +315,23 @@ template <> struct Tr<kQ6K> : Geo<kQ6K> {
     // the inversion applied to qh at load), converted with one signed-byte
     // convert and scaled by d*sc/4: exactly d*sc*(q-32), sign of zero
     // included.
-    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+    static __device__ __forceinline__ uint32_t bytes4(const Raw &r, int g) {
         const int t = g >> 2, G = g & 3;
         const uint32_t src = (t & 1) ? r.ql1[G] : r.ql0[G];
         const uint32_t lo = t < 2 ? ((src << 2) & 0x3C3C3C3Cu) : ((src >> 2) & 0x3C3C3C3Cu);
-        const uint32_t b = ((r.qhx[G] << (6 - 2 * t)) & 0xC0C0C0C0u) | lo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.ds4[t];
+        return ((r.qhx[G] << (6 - 2 * t)) & 0xC0C0C0C0u) | lo;
     }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+        const uint32_t b = bytes4(r, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.ds4[g >> 2];
+    }
+    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+        const uint32_t b = bytes4(r, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(b >> (8 * i));
+    }
+    static __device__ __forceinline__ float scale(const Pre &pr, int seg) { return pr.ds4[seg]; }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) {
         return 256 * (p >> 2) + 128 * ((p >> 1) & 1) + 32 * (g >> 2) + 16 * (p & 1) + 4 * (g & 3);
     }
@@ -437,21 +470,63 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
 #pragma unroll
     for (int r = 0; r < NR; ++r) pre[r] = TR::prep(raw[r], p);
     const float *__restrict__ xp = xs + TR::xoff(p, vb);
+    if constexpr (TR::SEG == 0) {
+        // unscaled: acc = fma(w, x, acc) value by value
 #pragma unroll
-    for (int g = 0; g < TR::NG; ++g) {
-        if (!TR::group_valid(p, g, k)) continue;
-        f32x4 xv[M];
+        for (int g = 0; g < TR::NG; ++g) {
+            if (!TR::group_valid(p, g, k)) continue;
+            f32x4 xv[M];
 #pragma unroll
-        for (int j = 0; j < M; ++j) xv[j] = *(const f32x4 *)(xp + j * XS + TR::goff(g));
+            for (int j = 0; j < M; ++j) xv[j] = *(const f32x4 *)(xp + j * XS + TR::goff(g));
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            float w[4];
-            TR::deq(raw[r], pre[r], g, w);
+            for (int r = 0; r < NR; ++r) {
+                float w[4];
+                TR::deq(raw[r], pre[r], g, w);
 #pragma unroll
-            for (int j = 0; j < M; ++j) {
+                for (int j = 0; j < M; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[r][j] = __builtin_fmaf(w[i], xv[j][i], acc[r][j]);
+                    for (int i = 0; i < 4; ++i) acc[r][j] = __builtin_fmaf(w[i], xv[j][i], acc[r][j]);
+                }
             }
+        }
+    } else {
+        // scaled: a segment's values share one scale s, so the segment
+        // contributes s * sum(q * x); the inner chain multiplies the exact
+        // integer-valued q, and one fma folds the segment into acc.  The x
+        // values of group g+1 are read while group g is multiplied, and the
+        // scheduler is kept from hoisting further reads (register pressure).
+        f32x4 xv[2][M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) xv[0][j] = *(const f32x4 *)(xp + j * XS + TR::goff(0));
+        float part[NR][M];
+#pragma unroll
+        for (int g = 0; g < TR::NG; ++g) {
+            const int gg = g % TR::SEG, cb = g & 1;
+            if (g + 1 < TR::NG) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) xv[cb ^ 1][j] = *(const f32x4 *)(xp + j * XS + TR::goff(g + 1));
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                float q[4];
+                TR::deqi(raw[r], g, q);
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        part[r][j] = (gg == 0 && i == 0) ? q[0] * xv[cb][j][0]
+                                                         : __builtin_fmaf(q[i], xv[cb][j][i], part[r][j]);
+                }
+            }
+            if (gg == TR::SEG - 1) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float sc = TR::scale(pre[r], g / TR::SEG);
+#pragma unroll
+                    for (int j = 0; j < M; ++j) acc[r][j] = __builtin_fmaf(sc, part[r][j], acc[r][j]);
+                }
+            }
+            if (M >= 4) __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
