@@ -10,9 +10,16 @@ time between two stream synchronisations around the replay.
 
 Prints one JSON line.  ``value`` is effective weight GB/s over the whole job
 (weight bytes of every call / wall time).  ``roofline`` is for the step's
-dominant kernel: algorithmic bytes per launch (weights + x + y) over its mean
-duration from HIP events on the bench stream.  ``cpu_baseline`` times the
-oracle (float64 CPU reference) on a bounded sample of the same workload.
+dominant (longest) kernel, whose mean duration comes from HIP events around
+back-to-back launches on the bench stream.  Its bound follows from its
+arithmetic intensity: below the ridge of the HBM roof (8 TB/s) and the FP32
+vector-ALU roof (256 CUs x 64 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s; the
+kernels use no packed FP32) it is "hbm" and ``achieved`` is algorithmic bytes
+(weights + x + y) per second; above it, "alu" and algorithmic flops (2nmk per
+batch) per second.  ``attainable_read`` is the fastest plain read of the same
+weight bytes (include/row_exact_probe.h), the practical ceiling for the
+weight stream at this size.  ``cpu_baseline`` times the oracle (float64 CPU
+reference) on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -26,6 +33,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+# FP32 FMA issue rate of the vector ALUs: 256 CUs x 64 lanes x 2 flops x 2.4 GHz.
+# (Packed FP32, which doubles it to the published 157.3 TFLOP/s, is not used:
+# the kernels are built with packed-FP32 selection off.)
+VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 METRIC = "effective weight GB/s and % of HBM peak, quantized GEMV at m=1/4/8"
 
 
@@ -135,17 +146,11 @@ def main():
         if rc:
             raise qfr.RowExactError(rc, qfr.row_exact_last_error())
 
-    def steps(first, count, events=None):
+    def steps(first, count):
         i = first
         for s in range(count):
             for m in ms:
-                if events is not None:
-                    events[m][0].append(torch.cuda.Event(enable_timing=True))
-                    events[m][1].append(torch.cuda.Event(enable_timing=True))
-                    events[m][0][-1].record(stream)
                 launch(i, m)
-                if events is not None:
-                    events[m][1][-1].record(stream)
                 i += 1
         return i
 
@@ -160,17 +165,41 @@ def main():
         print(f"bench.py: profile-only run of {args.steps} steps of {args.workload} done", flush=True)
         return
 
-    # Per-kernel durations: HIP events around every launch of the timed steps,
-    # on the bench stream, eager.  A bounded spin kernel is queued first so
-    # that every launch and event is enqueued before the GPU reaches them:
-    # the kernels then run back to back and each event pair brackets one
-    # kernel, not the host's launch latency.
-    events = {m: ([], []) for m in ms}
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(2e8))
-        steps(i, args.steps, events)
-    torch.cuda.synchronize()
-    kernel_us = {m: float(np.mean([a.elapsed_time(b) for a, b in zip(*events[m])]) * 1e3) for m in ms}
+    # Per-kernel durations: for each m, the timed number of launches back to
+    # back on the bench stream (cycling the weight copies) between one pair of
+    # HIP events, queued behind a bounded spin kernel so that the GPU never
+    # waits for the host; the mean launch duration is the span over the count.
+    kernel_us = {}
+    for m in ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(2e8))
+            e0.record(stream)
+            for s_ in range(args.steps):
+                launch(i + s_, m)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_us[m] = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    # Attainable read rate for this many bytes: a plain read of the same cold
+    # weight copies (include/row_exact_probe.h), fastest launch shape.
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rbytes = wbytes // 16 * 16
+    read_us = []
+    for shape in range(qfr.row_exact_stream_read_shapes()):
+        reps = max(2 * copies, 50)
+        with torch.cuda.stream(stream):
+            for r in range(copies):
+                qfr.row_exact_stream_read(wptrs[r], rbytes, sink.data_ptr(), shape, stream=hs)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(2e8))
+            e0.record(stream)
+            for r in range(reps):
+                qfr.row_exact_stream_read(wptrs[r % copies], rbytes, sink.data_ptr(), shape, stream=hs)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        read_us.append(e0.elapsed_time(e1) * 1e3 / reps)
+    attainable = rbytes / (min(read_us) * 1e-6) / 1e9
 
     # Whole-job timing: graph replay of the same K steps (or eager with --eager).
     y_eager = {m: ybufs[m].clone() for m in ms}
@@ -202,7 +231,14 @@ def main():
     dom = max(ms, key=lambda m: kernel_us[m])
     _, xb_dom, yb_dom = qfr.row_exact_required_bytes(t, n, k, dom, batch, strides)
     alg_bytes = wbytes + xb_dom + yb_dom
-    achieved = alg_bytes / (kernel_us[dom] * 1e-6) / 1e9
+    flops = {mm: 2.0 * n * k * mm * batch for mm in ms}
+    ridge = VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flops per byte where the two roofs meet
+    if flops[dom] / alg_bytes > ridge:
+        bound, unit, peak = "alu", "TFLOP/s", round(VALU_PEAK_TFLOPS, 1)
+        achieved = flops[dom] / (kernel_us[dom] * 1e-6) / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = alg_bytes / (kernel_us[dom] * 1e-6) / 1e9
 
     out = {
         "metric": METRIC,
@@ -223,16 +259,22 @@ def main():
             "parallelism": "single GPU",
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "attainable_read": {"GBps": round(attainable, 1), "bytes": rbytes, "us": round(min(read_us), 3),
+                            "hbm_frac": round(attainable / HBM_PEAK_GBS, 4)},
         "per_m": {str(m): {"kernel_us": round(kernel_us[m], 3),
                            "weight_GBps": round(wbytes / (kernel_us[m] * 1e-6) / 1e9, 1),
-                           "hbm_frac": round(wbytes / (kernel_us[m] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                           "hbm_frac": round(wbytes / (kernel_us[m] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                           "frac_of_attainable_read": round(min(read_us) / kernel_us[m], 4),
+                           "valu_TFLOPs": round(flops[m] / (kernel_us[m] * 1e-6) / 1e12, 2),
+                           "valu_frac": round(flops[m] / (kernel_us[m] * 1e-6) / 1e12 / VALU_PEAK_TFLOPS, 4)}
                   for m in ms},
         "kernel_source_hash": kernel_source_hash(),
         "roofline": {
             "kernel": f"mv_kernel<{wl.TYPE_NAMES[t]}, m={dom}>",
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
-            "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_us": round(kernel_us[dom], 3),
+            "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload, dom),
+            "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops[dom],
+            "mean_launch_us": round(kernel_us[dom], 3),
         },
     }
     if not args.no_cpu_baseline:
@@ -271,14 +313,16 @@ def cpu_baseline(w, W, x, ms, seconds):
 
 
 def sweep(path, steps):
-    """Mean kernel time of every (workload, m) with cold weights, HIP events
-    around each eager launch."""
+    """Mean kernel time of every (workload, m) with cold weights (one pair of
+    HIP events around back-to-back launches queued behind a spin kernel), next
+    to the attainable read time of the same bytes."""
     import numpy as np
     import torch
 
     import quantized_few_row_amd as qfr
     import workloads as wl
     res = []
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     for w in wl.WORKLOADS:
         t, n, k, batch = w.wtype, w.n, w.k, w.batch
         xrs, xbs, yrs, ybs = w.strides(8)
@@ -287,24 +331,39 @@ def sweep(path, steps):
         copies = max(2, int(np.ceil((1 << 30) / w.weight_bytes)))
         Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
         xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        rbytes = w.weight_bytes // 16 * 16
+        reps = min(steps, 200)
+
+        def span_us(fn):
+            """Mean duration of reps back-to-back launches of fn(i)."""
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(int(2e8))
+            a.record()
+            for i in range(reps):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / reps
+
+        read_us = []
+        for shape in range(qfr.row_exact_stream_read_shapes()):
+            for i in range(min(copies, 64)):
+                qfr.row_exact_stream_read(Wd[i], rbytes, sink, shape)
+            read_us.append(span_us(lambda i: qfr.row_exact_stream_read(Wd[i % copies], rbytes, sink, shape)))
         for m in sorted(set(w.ms) | {1, 4, 8}):
             _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, s)
             y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
             for i in range(10):
                 qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
-            ev = []
-            for i in range(min(steps, 200)):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
-                b.record()
-                ev.append((a, b))
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) for a, b in ev]) * 1e3)
+            us = span_us(lambda i: qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s))
             sch = qfr.row_exact_schedule(t, n, k, m, batch)
+            fl = 2.0 * n * k * m * batch
             res.append({"workload": w.name, "m": m, "kernel_us": round(us, 3),
                         "weight_GBps": round(w.weight_bytes / us / 1e3, 1),
                         "hbm_frac": round(w.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "attainable_read_us": round(min(read_us), 3),
+                        "frac_of_attainable_read": round(min(read_us) / us, 4),
+                        "valu_frac": round(fl / (us * 1e-6) / 1e12 / VALU_PEAK_TFLOPS, 4),
                         "schedule": sch.asdict()})
             print(json.dumps(res[-1]), file=sys.stderr, flush=True)
         del Wd

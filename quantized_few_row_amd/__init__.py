@@ -20,6 +20,7 @@ __all__ = [
     "contiguous", "grouped_token_major", "library_path", "load_library",
     "row_exact_mv", "row_exact_mv_scheduled", "row_exact_schedule", "row_exact_row_bytes",
     "row_exact_required_bytes", "row_exact_dequant", "row_exact_last_error", "row_exact_launch_count",
+    "row_exact_stream_read", "row_exact_stream_read_shapes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -122,6 +123,10 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_last_error.argtypes = []
     lib.row_exact_launch_count.restype = u64
     lib.row_exact_launch_count.argtypes = []
+    lib.row_exact_stream_read.restype = ctypes.c_int
+    lib.row_exact_stream_read.argtypes = [P, u64, P, u32, P]
+    lib.row_exact_stream_read_shapes.restype = u32
+    lib.row_exact_stream_read_shapes.argtypes = []
     _lib = lib
     return lib
 
@@ -240,3 +245,20 @@ def row_exact_last_error() -> str:
 
 def row_exact_launch_count() -> int:
     return int(load_library().row_exact_launch_count())
+
+
+def row_exact_stream_read_shapes() -> int:
+    """Launch shapes the read probe accepts (``include/row_exact_probe.h``)."""
+    return int(load_library().row_exact_stream_read_shapes())
+
+
+def row_exact_stream_read(W: Any, nbytes: int, sink: Any, shape: int = 0, stream: Any = None) -> None:
+    """Enqueue a plain read of ``nbytes`` of ``W`` (the attainable-read-rate
+    probe of ``include/row_exact_probe.h``; not part of the mat-vec)."""
+    wp, wlen = _ptr_and_bytes(W, "buffer")
+    sp, slen = _ptr_and_bytes(sink, "sink")
+    if wlen is not None and wlen < nbytes:
+        raise ValueError(f"buffer holds {wlen} bytes, {nbytes} requested")
+    if slen is not None and slen < 4:
+        raise ValueError("sink must hold 4 bytes")
+    _check(load_library().row_exact_stream_read(wp, nbytes, sp, shape, _stream_handle(stream)))

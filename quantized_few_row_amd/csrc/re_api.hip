@@ -31,6 +31,14 @@ int fail(int code, const char *fmt, ...) {
     return code;
 }
 
+}  // namespace
+
+// Shared with the other host translation units of the library.
+int rex::report_error(int code, const char *msg) { return fail(code, "%s", msg); }
+void rex::count_launch() { g_launches.fetch_add(1, std::memory_order_relaxed); }
+
+namespace {
+
 const char *type_name(int t) {
     static const char *names[] = {"F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0"};
     return (t >= 0 && t <= 4) ? names[t] : "?";

@@ -108,4 +108,9 @@ hipError_t launch_dq_q4_k(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q6_k(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q5_0(const DqArgs &, hipStream_t);
 
+// Error text for row_exact_last_error() (returns code) and the launch
+// counter, shared by every host translation unit of the library.
+int report_error(int code, const char *msg);
+void count_launch();
+
 }  // namespace rex

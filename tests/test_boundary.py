@@ -36,7 +36,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = qfr.load_library()
     declared = _declared_functions()
-    assert len(declared) == 8, declared
+    assert len(declared) == 10, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -196,3 +196,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(qfr, "_LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(qfr.LibraryMissing):
         qfr.row_exact_row_bytes(1, 32)
+
+
+def test_stream_read_probe_rejects_bad_arguments():
+    lib = qfr.load_library()
+    assert lib.row_exact_stream_read_shapes() >= 1
+    cases = [
+        ((0, 1024, YP, 0), -1),                 # NULL buffer
+        ((WP, 1024, 0, 0), -1),                 # NULL sink
+        ((WP, 0, YP, 0), -1),                   # empty
+        ((WP, 1000, YP, 0), -1),                # not a multiple of 16
+        ((WP, 1024, YP, 99), -1),               # unknown shape
+        ((WP + 8, 1024, YP, 0), -2),            # misaligned buffer
+        ((WP, 1024, YP + 2, 0), -2),            # misaligned sink
+    ]
+    before = qfr.row_exact_launch_count()
+    for args, code in cases:
+        assert lib.row_exact_stream_read(*args, None) == code, args
+        assert "stream_read" in qfr.row_exact_last_error()
+    assert qfr.row_exact_launch_count() == before

@@ -1,7 +1,7 @@
 """GPU parity of the HIP path against the oracle, at oracle-friendly sizes
 that span several wave steps and end in a ragged tail.
 
-Conditions checked (spec contract of the row-exact mat-vec):
+Conditions checked (the acceptance conditions of the row-exact mat-vec):
   1. row_exact_dequant output is bit-identical to the oracle's weights;
   2. |y - y_ref| <= 1e-5 * sum|w x| + 1e-6 against the float64 oracle;
   3. row j of an m-row call is bitwise the m = 1 call on row j
