@@ -9,6 +9,10 @@
  * module docs (the product, "Row exactness", "Batched / grouped products"),
  * RowExactWeight, RowExactMatvecShape, RowExactMatvecSchedule, validate(),
  * dispatch_row_exact_matvec and dispatch_row_exact_matvec_scheduled.
+ * Dense float32 and bfloat16 weights (ROW_EXACT_F32, ROW_EXACT_BF16) carry
+ * the same contract: nuvec-core 0.6.0, src/gpu.rs, the matmul routing of
+ * "a few rows" to gemv_rows, whose every row has the bits of its one-row
+ * product (the row-independence contract).
  *
  * Row exactness: output row j is bitwise identical whether it is computed with
  * m = 1 or as one row of any m <= 8, and identical across repeated calls.  The
@@ -51,6 +55,9 @@ extern "C" {
  *         k % 256 == 0; W 4-byte aligned.
  *  Q5_0 : row-major [batch*n, k/32] blocks of 22 bytes (f16 d, 32 high bits,
  *         16 bytes of nibbles); k % 32 == 0; W 4-byte aligned.
+ *  F32  : row-major [batch*n, k] IEEE single; k % 4 == 0; W 16-byte aligned.
+ *  BF16 : row-major [batch*n, k] bfloat16 (the upper 16 bits of an IEEE
+ *         single); k % 4 == 0; W 8-byte aligned.
  * Block layouts are those of the GGML types of the same names (the pages give
  * their byte sizes only).  The page's dispatcher accepts 2-byte-aligned
  * Q8_0 / Q6_K / Q5_0 weights; this library reads them with dword loads and
@@ -60,7 +67,9 @@ typedef enum {
     ROW_EXACT_Q8_0 = 1,
     ROW_EXACT_Q4_K = 2,
     ROW_EXACT_Q6_K = 3,
-    ROW_EXACT_Q5_0 = 4
+    ROW_EXACT_Q5_0 = 4,
+    ROW_EXACT_F32 = 5,
+    ROW_EXACT_BF16 = 6
 } row_exact_weight_t;
 
 /* Maximum input rows per call (ROW_EXACT_MATVEC_MAX_ROWS). */
@@ -91,8 +100,9 @@ typedef struct {
  *  workgroups_per_batch : packing.  Grid x; batch is grid y (batch-major).
  *  k_chunk              : packing.  Input values per row staged in LDS per
  *                         pass; >= k means one pass.  Otherwise a multiple of
- *                         the weight type's wave step (512 values for F16,
- *                         2048 for Q8_0 / Q5_0, 4096 for Q4_K / Q6_K).
+ *                         the weight type's wave step (512 values for F16 /
+ *                         BF16, 256 for F32, 2048 for Q8_0 / Q5_0, 4096 for
+ *                         Q4_K / Q6_K).
  * Packing fields never change the bits of y. */
 typedef struct {
     uint32_t k_split;
@@ -146,7 +156,8 @@ int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m
                        row_exact_schedule_t *out);
 
 /* Bytes per weight row of k values (RowExactWeight::row_bytes):
- * F16 2k; Q8_0 34*(k/32); Q4_K 144*(k/256); Q6_K 210*(k/256); Q5_0 22*(k/32).
+ * F16 2k; Q8_0 34*(k/32); Q4_K 144*(k/256); Q6_K 210*(k/256); Q5_0 22*(k/32);
+ * F32 4k; BF16 2k.
  * Returns 0 for an unknown type. */
 uint64_t row_exact_row_bytes(row_exact_weight_t wt, uint32_t k);
 

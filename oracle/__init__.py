@@ -9,8 +9,9 @@ The arithmetic lives in ``row_exact_oracle.c`` (plain C, built with gcc).
 This module only marshals numpy arrays in and out.
 
 What it computes (mlx-native 0.18.0, ``src/ops/row_exact_matvec.rs``, module
-docs and "Batched / grouped products"): for batch ``b``, input row ``j`` and
-output ``i``,
+docs and "Batched / grouped products"; for dense float32 / bfloat16 weights
+the same product under nuvec-core 0.6.0 ``src/gpu.rs``'s row-independence
+contract of ``gemv_rows``): for batch ``b``, input row ``j`` and output ``i``,
 ``y[b, j, i] = sum_kk Wd[b*n + i, kk] * x[b*xbs + j*xrs + kk]`` and
 ``a[b, j, i] = sum_kk |Wd[b*n + i, kk] * x[...]|``, both in float64, where
 ``Wd`` is the exact float32 value of each weight decoded from its block.
@@ -31,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "row_exact_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F16, Q8_0, Q4_K, Q6_K, Q5_0 = 0, 1, 2, 3, 4
+F16, Q8_0, Q4_K, Q6_K, Q5_0, F32, BF16 = 0, 1, 2, 3, 4, 5, 6
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -54,6 +55,10 @@ def _load() -> ctypes.CDLL:
         u32 = ctypes.c_uint32
         lib.oracle_f16_to_f32.restype = ctypes.c_float
         lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f32.restype = ctypes.c_float
+        lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.oracle_f32_from_bits.restype = ctypes.c_float
+        lib.oracle_f32_from_bits.argtypes = [ctypes.c_uint32]
         lib.oracle_row_bytes.restype = ctypes.c_uint64
         lib.oracle_row_bytes.argtypes = [ctypes.c_int, u32]
         lib.oracle_weight.restype = ctypes.c_float
@@ -77,6 +82,26 @@ def f16_to_f32(bits: np.ndarray) -> np.ndarray:
     out = np.empty(flat.size, dtype=np.float32)
     for i, b in enumerate(flat.tolist()):
         out[i] = lib.oracle_f16_to_f32(b)
+    return out.reshape(np.shape(bits))
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Decode uint16 bfloat16 bit patterns (one call per value)."""
+    lib = _load()
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    out = np.empty(flat.size, dtype=np.float32)
+    for i, b in enumerate(flat.tolist()):
+        out[i] = lib.oracle_bf16_to_f32(b)
+    return out.reshape(np.shape(bits))
+
+
+def f32_from_bits(bits: np.ndarray) -> np.ndarray:
+    """Decode uint32 binary32 bit patterns (one call per value)."""
+    lib = _load()
+    flat = np.asarray(bits, dtype=np.uint32).ravel()
+    out = np.empty(flat.size, dtype=np.float32)
+    for i, b in enumerate(flat.tolist()):
+        out[i] = lib.oracle_f32_from_bits(b)
     return out.reshape(np.shape(bits))
 
 

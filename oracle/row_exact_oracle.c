@@ -14,6 +14,10 @@
  *     b * y_batch_stride;
  *   - the block constants (32 values / 34 bytes, 256 / 144, 256 / 210,
  *     32 / 22) and RowExactWeight::row_bytes.
+ * Dense float32 and bfloat16 weights follow the same product (nuvec-core
+ * 0.6.0, src/gpu.rs: the matmul's "a few rows" route to gemv_rows and its
+ * row-independence contract); their values are decoded from the IEEE fields.
+ *
  * The pages give block byte sizes only.  The bit layout inside each block is
  * the plain reading of the GGML types the enum is named after; every value is
  * decoded on its own, from its index, straight from that layout.
@@ -29,7 +33,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_0 = 4 };
+enum { OR_F16 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_0 = 4, OR_F32 = 5, OR_BF16 = 6 };
 
 static uint16_t rd_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
@@ -55,6 +59,42 @@ float oracle_f16_to_f32(uint16_t h) {
     return (float)(sign ? -v : v);
 }
 
+/* bfloat16 -> float, from the definition: sign, 8-bit exponent (bias 127),
+ * 7-bit fraction; exponent 0 is zero/subnormal (f * 2^-133), exponent 255 is
+ * infinity/NaN. */
+float oracle_bf16_to_f32(uint16_t h) {
+    int sign = h >> 15;
+    int e = (h >> 7) & 255;
+    int f = h & 127;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -133);
+    } else if (e == 255) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + f), e - 134);
+    }
+    return (float)(sign ? -v : v);
+}
+
+/* IEEE 754 binary32 bit pattern -> float, from the definition: sign, 8-bit
+ * exponent (bias 127), 23-bit fraction; exponent 0 is zero/subnormal
+ * (f * 2^-149), exponent 255 is infinity/NaN. */
+float oracle_f32_from_bits(uint32_t u) {
+    int sign = (int)(u >> 31);
+    int e = (int)((u >> 23) & 255u);
+    uint32_t f = u & 0x7FFFFFu;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -149);
+    } else if (e == 255) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(0x800000u + f), e - 150);
+    }
+    return (float)(sign ? -v : v);
+}
+
 /* Bytes per row of k values (RowExactWeight::row_bytes). */
 uint64_t oracle_row_bytes(int type, uint32_t k) {
     switch (type) {
@@ -63,6 +103,8 @@ uint64_t oracle_row_bytes(int type, uint32_t k) {
     case OR_Q4_K: return (uint64_t)(k / 256) * 144;
     case OR_Q6_K: return (uint64_t)(k / 256) * 210;
     case OR_Q5_0: return (uint64_t)(k / 32) * 22;
+    case OR_F32: return (uint64_t)k * 4;
+    case OR_BF16: return (uint64_t)k * 2;
     default: return 0;
     }
 }
@@ -145,6 +187,10 @@ static float value_q6_k(const uint8_t *row, uint32_t v) {
 
 static float value_f16(const uint8_t *row, uint32_t v) { return oracle_f16_to_f32(rd_u16(row + 2 * (size_t)v)); }
 
+static float value_f32(const uint8_t *row, uint32_t v) { return oracle_f32_from_bits(rd_u32(row + 4 * (size_t)v)); }
+
+static float value_bf16(const uint8_t *row, uint32_t v) { return oracle_bf16_to_f32(rd_u16(row + 2 * (size_t)v)); }
+
 /* Exact float32 value of weight v of one row. */
 float oracle_weight(int type, const uint8_t *row, uint32_t v) {
     switch (type) {
@@ -153,13 +199,15 @@ float oracle_weight(int type, const uint8_t *row, uint32_t v) {
     case OR_Q4_K: return value_q4_k(row, v);
     case OR_Q6_K: return value_q6_k(row, v);
     case OR_Q5_0: return value_q5_0(row, v);
+    case OR_F32: return value_f32(row, v);
+    case OR_BF16: return value_bf16(row, v);
     default: return NAN;
     }
 }
 
 static int k_ok(int type, uint32_t k) {
     switch (type) {
-    case OR_F16: return k % 4 == 0;
+    case OR_F16: case OR_F32: case OR_BF16: return k % 4 == 0;
     case OR_Q8_0: case OR_Q5_0: return k % 32 == 0;
     case OR_Q4_K: case OR_Q6_K: return k % 256 == 0;
     default: return 0;

@@ -38,6 +38,8 @@ class Weight(enum.IntEnum):
     Q4_K = 2
     Q6_K = 3
     Q5_0 = 4
+    F32 = 5
+    BF16 = 6
 
 
 class Strides(ctypes.Structure):
@@ -160,7 +162,7 @@ def _dtype_check(wt: Weight, W: Any, x: Any, y: Any) -> None:
     if isinstance(W, int):
         return
     import torch
-    want = torch.float16 if wt == Weight.F16 else torch.uint8
+    want = {Weight.F16: torch.float16, Weight.F32: torch.float32, Weight.BF16: torch.bfloat16}.get(wt, torch.uint8)
     if W.dtype not in (want, torch.uint8):
         raise ValueError(f"{wt.name} weight must be {want} (or raw uint8 bytes), got {W.dtype}")
     for t, name in ((x, "x"), (y, "y")):

@@ -40,25 +40,26 @@ void rex::count_launch() { g_launches.fetch_add(1, std::memory_order_relaxed); }
 namespace {
 
 const char *type_name(int t) {
-    static const char *names[] = {"F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0"};
-    return (t >= 0 && t <= 4) ? names[t] : "?";
+    static const char *names[] = {"F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0", "F32", "BF16"};
+    return (t >= 0 && t < kNumTypes) ? names[t] : "?";
 }
 
-bool valid_type(int t) { return t >= 0 && t <= 4; }
+bool valid_type(int t) { return t >= 0 && t < kNumTypes; }
 
 uint32_t k_multiple(int t) {
     switch (t) {
-    case kF16: return 4;
+    case kF16: case kF32: case kBF16: return 4;
     case kQ8_0: case kQ5_0: return 32;
     default: return 256;
     }
 }
 
-// Weight pointer alignment this library needs (the page asks 8 / 2 / 16 / 2 / 2).
+// Weight pointer alignment this library needs (the page asks 8 / 2 / 16 / 2 / 2
+// for its five types; F32 rows are read 16 bytes at a time, BF16 as F16).
 uint32_t w_align(int t) {
     switch (t) {
-    case kF16: return 8;
-    case kQ4K: return 16;
+    case kF16: case kBF16: return 8;
+    case kQ4K: case kF32: return 16;
     default: return 4;
     }
 }
@@ -70,6 +71,8 @@ uint64_t row_bytes_of(int t, uint32_t k) {
     case kQ4K: return (uint64_t)(k / 256) * 144;
     case kQ6K: return (uint64_t)(k / 256) * 210;
     case kQ5_0: return (uint64_t)(k / 32) * 22;
+    case kF32: return (uint64_t)k * 4;
+    case kBF16: return (uint64_t)k * 2;
     default: return 0;
     }
 }
@@ -208,6 +211,8 @@ MvAttributes mv_attributes(int t) {
     case kQ8_0: return attributes_mv_q8_0;
     case kQ4K: return attributes_mv_q4_k;
     case kQ6K: return attributes_mv_q6_k;
+    case kF32: return attributes_mv_f32;
+    case kBF16: return attributes_mv_bf16;
     default: return attributes_mv_q5_0;
     }
 }
@@ -333,6 +338,8 @@ MvLauncher mv_launcher(int t) {
     case kQ8_0: return launch_mv_q8_0;
     case kQ4K: return launch_mv_q4_k;
     case kQ6K: return launch_mv_q6_k;
+    case kF32: return launch_mv_f32;
+    case kBF16: return launch_mv_bf16;
     default: return launch_mv_q5_0;
     }
 }
@@ -343,6 +350,8 @@ DqLauncher dq_launcher(int t) {
     case kQ8_0: return launch_dq_q8_0;
     case kQ4K: return launch_dq_q4_k;
     case kQ6K: return launch_dq_q6_k;
+    case kF32: return launch_dq_f32;
+    case kBF16: return launch_dq_bf16;
     default: return launch_dq_q5_0;
     }
 }

@@ -6,7 +6,8 @@
 
 namespace rex {
 
-enum WeightType : int { kF16 = 0, kQ8_0 = 1, kQ4K = 2, kQ6K = 3, kQ5_0 = 4 };
+enum WeightType : int { kF16 = 0, kQ8_0 = 1, kQ4K = 2, kQ6K = 3, kQ5_0 = 4, kF32 = 5, kBF16 = 6 };
+constexpr int kNumTypes = 7;
 
 // Kernel argument block (passed by value).
 struct MvArgs {
@@ -56,6 +57,14 @@ template <> struct Geo<kQ5_0> {  // piece: one 22-byte block
     static constexpr int PV = 32, NG = 8, PADP = 32;
     __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 32; }
 };
+template <> struct Geo<kF32> {   // piece: 4 consecutive floats (16 bytes)
+    static constexpr int PV = 4, NG = 1, PADP = 32;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return k / 4; }
+};
+template <> struct Geo<kBF16> {  // piece: 8 consecutive bfloat16 (16 bytes)
+    static constexpr int PV = 8, NG = 2, PADP = 32;
+    __host__ __device__ static constexpr uint32_t pieces(uint32_t k) { return (k + 7) / 8; }
+};
 
 // Values covered by one wave step (64 pieces).
 inline uint32_t wave_step_values(int t) {
@@ -64,6 +73,8 @@ inline uint32_t wave_step_values(int t) {
     case kQ8_0: return 64 * Geo<kQ8_0>::PV;
     case kQ4K: return 64 * Geo<kQ4K>::PV;
     case kQ6K: return 64 * Geo<kQ6K>::PV;
+    case kF32: return 64 * Geo<kF32>::PV;
+    case kBF16: return 64 * Geo<kBF16>::PV;
     default: return 64 * Geo<kQ5_0>::PV;
     }
 }
@@ -73,6 +84,8 @@ inline uint32_t pieces_of(int t, uint32_t k) {
     case kQ8_0: return Geo<kQ8_0>::pieces(k);
     case kQ4K: return Geo<kQ4K>::pieces(k);
     case kQ6K: return Geo<kQ6K>::pieces(k);
+    case kF32: return Geo<kF32>::pieces(k);
+    case kBF16: return Geo<kBF16>::pieces(k);
     default: return Geo<kQ5_0>::pieces(k);
     }
 }
@@ -82,6 +95,8 @@ inline uint32_t pad_period(int t) {
     case kQ8_0: return Geo<kQ8_0>::PADP;
     case kQ4K: return Geo<kQ4K>::PADP;
     case kQ6K: return Geo<kQ6K>::PADP;
+    case kF32: return Geo<kF32>::PADP;
+    case kBF16: return Geo<kBF16>::PADP;
     default: return Geo<kQ5_0>::PADP;
     }
 }
@@ -97,16 +112,22 @@ hipError_t launch_mv_q8_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t
 hipError_t launch_mv_q4_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t launch_mv_q6_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t launch_mv_q5_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_f32(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_bf16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
 hipError_t attributes_mv_f16(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t attributes_mv_q8_0(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t attributes_mv_q4_k(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t attributes_mv_q6_k(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t attributes_mv_q5_0(uint32_t, uint32_t, hipFuncAttributes *);
+hipError_t attributes_mv_f32(uint32_t, uint32_t, hipFuncAttributes *);
+hipError_t attributes_mv_bf16(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t launch_dq_f16(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q8_0(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q4_k(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q6_k(const DqArgs &, hipStream_t);
 hipError_t launch_dq_q5_0(const DqArgs &, hipStream_t);
+hipError_t launch_dq_f32(const DqArgs &, hipStream_t);
+hipError_t launch_dq_bf16(const DqArgs &, hipStream_t);
 
 // Error text for row_exact_last_error() (returns code) and the launch
 // counter, shared by every host translation unit of the library.

@@ -131,6 +131,62 @@ template <> struct Tr<kF16> : Geo<kF16> {
     }
 };
 
+// ---------------------------------------------------------------- BF16
+// Piece p: values 8p..8p+7 (16 bytes), as F16.  A bfloat16 is the upper half
+// of a float32, so the exact widening is a 16-bit shift.
+template <> struct Tr<kBF16> : Geo<kBF16> {
+    static constexpr int SEG = 0;
+    struct Raw { uint32_t w[4]; };
+    struct Pre {};
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t k) {
+        const auto h = Tr<kF16>::load(R, o0, p, k);
+        Raw r;
+        r.w[0] = h.w[0]; r.w[1] = h.w[1]; r.w[2] = h.w[2]; r.w[3] = h.w[3];
+        return r;
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &, uint32_t) { return {}; }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &, int g, float (&w)[4]) {
+        w[0] = __uint_as_float(r.w[2 * g] << 16);
+        w[1] = __uint_as_float(r.w[2 * g] & 0xffff0000u);
+        w[2] = __uint_as_float(r.w[2 * g + 1] << 16);
+        w[3] = __uint_as_float(r.w[2 * g + 1] & 0xffff0000u);
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return Tr<kF16>::vpos(p, g); }
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) { return Tr<kF16>::xoff(p, vb); }
+    static constexpr uint32_t goff(int g) { return 4 * g; }
+    static __device__ __forceinline__ bool group_valid(uint32_t p, int g, uint32_t k) {
+        return Tr<kF16>::group_valid(p, g, k);
+    }
+};
+
+// ---------------------------------------------------------------- F32
+// Piece p: values 4p..4p+3 (16 bytes, 16-byte aligned: W is, and a row is
+// 4k bytes with k % 4 == 0).
+template <> struct Tr<kF32> : Geo<kF32> {
+    static constexpr int SEG = 0;
+    struct Raw { uint32_t w[4]; };
+    struct Pre {};
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        const u32x4 v = ldv<u32x4>(R, o0 + 16 * p);
+        Raw r;
+        r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+        return r;
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &, uint32_t) { return {}; }
+    static __device__ __forceinline__ void deq(const Raw &r, const Pre &, int, float (&w)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __uint_as_float(r.w[i]);
+    }
+    static __device__ __forceinline__ uint32_t vpos(uint32_t p, int) { return 4 * p; }
+    // PADP 32: 4 pad floats after every 8 pieces
+    static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
+        const uint32_t q = p - vb / 4;
+        return 4 * q + 4 * (q / 8);
+    }
+    static constexpr uint32_t goff(int) { return 0; }
+    static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
+};
+
 // ---------------------------------------------------------------- Q8_0
 // Piece p: block p (34 bytes: f16 d, 32 int8).  w = d * q.
 template <> struct Tr<kQ8_0> : Geo<kQ8_0> {

@@ -1,0 +1,17 @@
+// Mat-vec and dequant kernels for one weight type (instantiations only; the
+// device code is in re_kernels.h).
+#include "re_kernels.h"
+
+namespace rex {
+
+hipError_t launch_mv_f32(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    return launch_mv<kF32>(a, m, nr, grid, block, lds, s);
+}
+
+hipError_t attributes_mv_f32(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {
+    return attributes_mv<kF32>(m, nr, attr);
+}
+
+hipError_t launch_dq_f32(const DqArgs &a, hipStream_t s) { return launch_dq<kF32>(a, s); }
+
+}  // namespace rex

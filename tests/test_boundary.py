@@ -54,11 +54,14 @@ def test_row_bytes_match_page():
         for nb in (1, 3, 16, 56):
             assert qfr.row_exact_row_bytes(Weight[name], blk["values"] * nb) == blk["bytes"] * nb
     assert qfr.row_exact_row_bytes(Weight.F16, 512) == 1024
+    assert qfr.row_exact_row_bytes(Weight.F32, 512) == 2048
+    assert qfr.row_exact_row_bytes(Weight.BF16, 512) == 1024
     assert qfr.row_exact_row_bytes(7, 512) == 0
 
 
 def test_weight_order_matches_page():
-    assert [w.name for w in Weight] == GOLDEN["weight_type_order"]["value"]
+    # the page's five types in its index() order, then the dense extension
+    assert [w.name for w in Weight] == GOLDEN["weight_type_order"]["value"] + ["F32", "BF16"]
     assert qfr.MAX_ROWS == GOLDEN["max_rows"]["value"]
 
 
@@ -103,12 +106,15 @@ def _mv(wt=Weight.Q8_0, W=WP, x=XP, y=YP, n=64, k=256, m=4, batch=1, strides=Non
     (dict(n=0), -1, "must be > 0"),
     (dict(k=0), -1, "must be > 0"),
     (dict(batch=0), -1, "must be > 0"),
-    (dict(wt=5), -1, "unknown weight type"),
+    (dict(wt=7), -1, "unknown weight type"),
+    (dict(wt=-1), -1, "unknown weight type"),
     (dict(wt=Weight.Q8_0, k=48), -1, "multiple of 32"),
     (dict(wt=Weight.Q4_K, k=512 + 32), -1, "multiple of 256"),
     (dict(wt=Weight.Q6_K, k=128), -1, "multiple of 256"),
     (dict(wt=Weight.Q5_0, k=16), -1, "multiple of 32"),
     (dict(wt=Weight.F16, k=6), -1, "multiple of 4"),
+    (dict(wt=Weight.F32, k=10), -1, "multiple of 4"),
+    (dict(wt=Weight.BF16, k=2), -1, "multiple of 4"),
     (dict(W=0), -1, "non-NULL"),
     (dict(y=0), -1, "non-NULL"),
     (dict(x=XP + 4), -2, "16-byte aligned"),
@@ -116,6 +122,8 @@ def _mv(wt=Weight.Q8_0, W=WP, x=XP, y=YP, n=64, k=256, m=4, batch=1, strides=Non
     (dict(strides=Strides(256, 2, 64, 0), batch=2), -3, "multiples of 4"),
     (dict(wt=Weight.Q4_K, W=WP + 4), -2, "16-byte"),
     (dict(wt=Weight.F16, W=WP + 4, k=64), -2, "8-byte"),
+    (dict(wt=Weight.BF16, W=WP + 4, k=64), -2, "8-byte"),
+    (dict(wt=Weight.F32, W=WP + 8, k=64), -2, "16-byte"),
     (dict(wt=Weight.Q8_0, W=WP + 2), -2, "4-byte"),
     (dict(y=YP + 2), -2, "4-byte aligned"),
 ])

@@ -30,6 +30,8 @@ SHAPES = {
     wl.Q4_K: (67, 4352),   # 17 super-blocks = 68 pieces
     wl.Q6_K: (41, 4352),   # 17 super-blocks = 68 pieces
     wl.Q5_0: (53, 2112),   # 66 blocks
+    wl.F32: (69, 1028),    # 257 pieces of 4 values: 4 wave steps and one piece
+    wl.BF16: (77, 1028),   # as F16
 }
 TYPES = list(SHAPES)
 IDS = [wl.TYPE_NAMES[t] for t in TYPES]
@@ -82,7 +84,7 @@ def test_repeat_bitwise(t, data):
 
 
 def _schedules(t, k):
-    step = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048}[t]
+    step = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048, wl.F32: 256, wl.BF16: 512}[t]
     out = []
     for nr in (1, 2, 4):
         for waves, wgs in ((1, 1), (1, 1000), (4, 3), (8, 2), (8, 64), (3, 5)):
@@ -106,7 +108,7 @@ def test_packing_is_inert(t, m, data):
 
 @pytest.mark.parametrize("t", TYPES, ids=IDS)
 def test_ragged_n_and_minimal_k(t):
-    kmin = {wl.F16: 4, wl.Q8_0: 32, wl.Q4_K: 256, wl.Q6_K: 256, wl.Q5_0: 32}[t]
+    kmin = {wl.F16: 4, wl.Q8_0: 32, wl.Q4_K: 256, wl.Q6_K: 256, wl.Q5_0: 32, wl.F32: 4, wl.BF16: 4}[t]
     for n in (1, 2, 3, 5, 7, 9, 63, 65):
         for k in (kmin, kmin * 3):
             W = wl.weights(t, n, k, seed=500 + n + k)
@@ -120,7 +122,8 @@ def test_ragged_n_and_minimal_k(t):
 def test_strided_batched_with_gaps(t):
     """Batch-major and token-major strided layouts; elements outside the
     view keep their sentinel."""
-    n, k = 37, {wl.F16: 516, wl.Q8_0: 2080, wl.Q4_K: 2304, wl.Q6_K: 4352, wl.Q5_0: 2112}[t]
+    n, k = 37, {wl.F16: 516, wl.Q8_0: 2080, wl.Q4_K: 2304, wl.Q6_K: 4352, wl.Q5_0: 2112, wl.F32: 516,
+                wl.BF16: 516}[t]
     batch, m = 3, 4
     W = wl.weights(t, n * batch, k, seed=700 + t)
     for s in (Strides(k + 12, 5 * (k + 12), n + 3, 5 * (n + 3)),          # batch-major with gaps
@@ -169,7 +172,7 @@ def test_error_leaves_output_untouched(data):
 
 def test_default_schedule_properties():
     for t in TYPES:
-        for k in (512 if t == wl.F16 else 4096, 14336 if t in (wl.Q4_K, wl.Q6_K) else 8192):
+        for k in (512 if t in wl.DENSE else 4096, 14336 if t in (wl.Q4_K, wl.Q6_K) else 8192):
             splits = {qfr.row_exact_schedule(t, n, k, m).k_split for n in (64, 4096, 128256) for m in (1, 4, 8)}
             assert splits == {1}
             s = qfr.row_exact_schedule(t, 4096, k, 8)

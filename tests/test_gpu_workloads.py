@@ -1,4 +1,4 @@
-"""The five synthetic workloads at full size, in the launch configuration the
+"""The synthetic workloads at full size, in the launch configuration the
 benchmark times (the default schedule).  The oracle checks sampled output
 rows (first, last and seeded random ones) and sampled weight rows; row
 exactness and repeatability are checked on every output, GPU against GPU.

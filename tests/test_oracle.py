@@ -17,7 +17,8 @@ import workloads as wl
 from blockpack import (enc_f16, enc_q4_k, enc_q5_0, enc_q6_k, enc_q8_0, f16_bits, round_f32)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-TYPES = {"F16": wl.F16, "Q8_0": wl.Q8_0, "Q4_K": wl.Q4_K, "Q6_K": wl.Q6_K, "Q5_0": wl.Q5_0}
+TYPES = {"F16": wl.F16, "Q8_0": wl.Q8_0, "Q4_K": wl.Q4_K, "Q6_K": wl.Q6_K, "Q5_0": wl.Q5_0,
+         "F32": wl.F32, "BF16": wl.BF16}
 
 
 def _bits32(a):
@@ -36,14 +37,15 @@ def test_row_bytes_match_page_constants():
             assert oracle.row_bytes(TYPES[name], k) == blk["bytes"] * nblk
     for k in (4, 8, 512, 4096):
         assert oracle.row_bytes(wl.F16, k) == g["f16_bytes_per_value"]["value"] * k
+        assert oracle.row_bytes(wl.F32, k) == 4 * k and oracle.row_bytes(wl.BF16, k) == 2 * k
 
 
-@pytest.mark.parametrize("name", ["F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0"])
+@pytest.mark.parametrize("name", ["F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0", "F32", "BF16"])
 def test_row_locality(name):
     """Row r decodes from bytes [r*rb, (r+1)*rb) only: the parser consumes
     exactly row_bytes per row."""
     t = TYPES[name]
-    k = 512 if t != wl.F16 else 64
+    k = 64 if t in wl.DENSE else 512
     rows = 4
     W = wl.weights(t, rows, k, seed=11)
     full = oracle.dequant(t, W, rows, k)
@@ -70,6 +72,54 @@ def test_f16_exhaustive_against_numpy():
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(ours), nan)
     assert np.array_equal(_bits32(ours[~nan]), _bits32(ref[~nan]))
+
+
+def test_bf16_exhaustive_against_bit_widening():
+    """bfloat16 is the upper half of a binary32: numpy's reinterpretation of
+    the widened bits is the reference for all 65536 patterns."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.bf16_to_f32(bits)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(_bits32(ours[~nan]), _bits32(ref[~nan]))
+    # a few by hand: 1.0, -2.0, pi rounded, the smallest subnormal, -0
+    hand = oracle.bf16_to_f32(np.array([0x3F80, 0xC000, 0x4049, 0x0001, 0x8000], np.uint16))
+    assert hand[:3].tolist() == [1.0, -2.0, 3.140625] and hand[3] == 2.0 ** -133
+    assert _bits32(hand[4]) == 0x80000000
+
+
+def test_f32_decode_against_numpy():
+    rng = np.random.default_rng(5)
+    bits = np.concatenate([rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32),
+                           np.array([0, 1, 0x80000000, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0x3F800000,
+                                     0xFF7FFFFF, 0x7F800000, 0xFF800000], np.uint32)])
+    ours = oracle.f32_from_bits(bits)
+    ref = bits.view(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(_bits32(ours[~nan]), _bits32(ref[~nan]))
+
+
+def test_dense_weights_decode_as_numpy_views():
+    """F32 rows are float32 values as stored; BF16 rows widen bit for bit."""
+    for t in (wl.F32, wl.BF16):
+        W = wl.weights(t, 3, 36, seed=71)
+        d = oracle.dequant(t, W, 3, 36)
+        if t == wl.F32:
+            ref = W.ravel().view(np.float32).reshape(3, 36)
+        else:
+            ref = (W.ravel().view(np.uint16).astype(np.uint32) << 16).view(np.float32).reshape(3, 36)
+        assert np.array_equal(_bits32(d), _bits32(ref))
+
+
+def test_bf16_generator_rounds_to_nearest_even():
+    """The BF16 recipe rounds float32 to the nearest bfloat16, ties to even."""
+    from workloads import _bf16_bits
+    f = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -1.0 - 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20],
+                 np.float64)
+    got = (_bf16_bits(f).astype(np.uint32) << 16).view(np.float32)
+    assert got.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, 1.0, -1.0, 1.0 + 2 ** -7]
 
 
 # ---------------------------------------------------------------- hand-worked blocks
@@ -296,13 +346,13 @@ def _exact_dot(wd_row, x_row):
     return sum((Fraction(float(w)) * Fraction(float(v)) for w, v in zip(wd_row, x_row)), Fraction(0))
 
 
-@pytest.mark.parametrize("name", ["F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0"])
+@pytest.mark.parametrize("name", ["F16", "Q8_0", "Q4_K", "Q6_K", "Q5_0", "F32", "BF16"])
 def test_matvec_brute_force_strided_batched(name):
     """Exact rational dot on tiny strided, batched inputs: the oracle's float64
     sum is within k * 2^-53 * sum|w x| of the exact value, and |w x| sums
     likewise.  Junk in the stride gaps must not leak in."""
     t = TYPES[name]
-    k = {wl.F16: 12, wl.Q8_0: 64, wl.Q5_0: 64, wl.Q4_K: 256, wl.Q6_K: 256}[t]
+    k = {wl.F16: 12, wl.Q8_0: 64, wl.Q5_0: 64, wl.Q4_K: 256, wl.Q6_K: 256, wl.F32: 12, wl.BF16: 20}[t]
     n, m, batch = 3, 3, 2
     xrs, xbs = k + 8, 3 * (k + 8) + 4
     W = wl.weights(t, n * batch, k, seed=21)

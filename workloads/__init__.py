@@ -21,12 +21,13 @@ from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
-F16, Q8_0, Q4_K, Q6_K, Q5_0 = 0, 1, 2, 3, 4
-TYPE_NAMES = {F16: "F16", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_0: "Q5_0"}
+F16, Q8_0, Q4_K, Q6_K, Q5_0, F32, BF16 = 0, 1, 2, 3, 4, 5, 6
+TYPE_NAMES = {F16: "F16", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_0: "Q5_0", F32: "F32", BF16: "BF16"}
 NAME_TYPES = {v: k for k, v in TYPE_NAMES.items()}
 
 # (values per block, bytes per block)
-BLOCK = {F16: (1, 2), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q5_0: (32, 22)}
+BLOCK = {F16: (1, 2), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q5_0: (32, 22), F32: (1, 4), BF16: (1, 2)}
+DENSE = (F16, F32, BF16)
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
@@ -79,6 +80,14 @@ def _f16_bits(values: np.ndarray) -> np.ndarray:
     return values.astype(np.float16).view(np.uint16)
 
 
+def _bf16_bits(values: np.ndarray) -> np.ndarray:
+    """float64 -> float32 (nearest even) -> bfloat16 (nearest even on the
+    float32 bits; the values drawn here are finite)."""
+    u = values.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
 def _put_u16(blocks: np.ndarray, offset: int, bits: np.ndarray) -> None:
     blocks[:, offset] = (bits & 0xFF).astype(np.uint8)
     blocks[:, offset + 1] = (bits >> 8).astype(np.uint8)
@@ -89,6 +98,8 @@ def weights(wtype: int, rows: int, k: int, seed: int) -> np.ndarray:
     synthetic workload recipe:
 
     - F16: N(0, 0.02) rounded to half.
+    - F32: N(0, 0.02) rounded to float32.
+    - BF16: N(0, 0.02) rounded to float32, then to bfloat16 (nearest even).
     - Q8_0: d = half(|N(0,1)| * 0.01); 32 int8 uniform on [-127, 127].
     - Q4_K: d, dmin = half(|N(0,1)| * 0.01); 12 scale bytes and 128 quant bytes
       uniform (all 6-bit scales/mins and 4-bit quants uniform).
@@ -97,12 +108,18 @@ def weights(wtype: int, rows: int, k: int, seed: int) -> np.ndarray:
     - Q5_0: d = half(|N(0,1)| * 0.01); 4 high-bit and 16 nibble bytes uniform.
     """
     per, nbytes = BLOCK[wtype]
-    if k % (4 if wtype == F16 else per):
+    if k % (4 if wtype in DENSE else per):
         raise ValueError(f"k={k} is not a multiple of the block size of {TYPE_NAMES[wtype]}")
     s = Stream(seed)
     if wtype == F16:
         vals = s.normal(rows * k) * 0.02
         return _f16_bits(vals).view(np.uint8).reshape(rows, 2 * k).copy()
+    if wtype == F32:
+        vals = s.normal(rows * k) * 0.02
+        return vals.astype(np.float32).view(np.uint8).reshape(rows, 4 * k).copy()
+    if wtype == BF16:
+        vals = s.normal(rows * k) * 0.02
+        return _bf16_bits(vals).view(np.uint8).reshape(rows, 2 * k).copy()
     nblk = rows * (k // per)
     blocks = s.bytes(nblk * nbytes).reshape(nblk, nbytes)
     if wtype == Q8_0:
@@ -175,7 +192,7 @@ class Workload:
         return activations(8, cols, self.x_seed)[:m].copy()
 
 
-# The five workload configurations of the row-exact mat-vec (index = seed offset).
+# The workload configurations of the row-exact mat-vec (index = seed offset).
 WORKLOADS: List[Workload] = [
     Workload("f16_256x512", F16, 256, 512, 1, tuple(range(1, 9)), 0),
     Workload("q8_0_4096x4096", Q8_0, 4096, 4096, 1, (1, 4, 8), 1),
@@ -183,6 +200,9 @@ WORKLOADS: List[Workload] = [
     Workload("q6_k_4096x14336", Q6_K, 4096, 14336, 1, (1, 8), 3),
     Workload("q6_k_128256x4096", Q6_K, 128256, 4096, 1, (1, 8), 4),
     Workload("q5_0_16x1024x4096_grouped", Q5_0, 1024, 4096, 16, (8,), 5, grouped=True),
+    # dense weights under the same contract (a 4096 x 4096 projection)
+    Workload("f32_4096x4096", F32, 4096, 4096, 1, (1, 4, 8), 6),
+    Workload("bf16_4096x4096", BF16, 4096, 4096, 1, (1, 4, 8), 7),
 ]
 BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
 
