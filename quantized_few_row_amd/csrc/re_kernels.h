@@ -39,6 +39,17 @@
 
 #include "re_internal.h"
 
+// Code-generation knobs (measured defaults; variants with other values,
+// and with register caps for more waves per SIMD, measured no faster): the
+// smallest m whose piece loop gets a scheduling barrier per group, and the
+// register budget that allows two items of loads in flight.
+#ifndef REX_SCHED_BARRIER_MIN_M
+#define REX_SCHED_BARRIER_MIN_M 4
+#endif
+#ifndef REX_DEPTH_BUDGET
+#define REX_DEPTH_BUDGET 120
+#endif
+
 namespace rex {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -582,7 +593,7 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
                     for (int j = 0; j < M; ++j) acc[r][j] = __builtin_fmaf(sc, part[r][j], acc[r][j]);
                 }
             }
-            if (M >= 4) __builtin_amdgcn_sched_barrier(0);
+            if (M >= REX_SCHED_BARRIER_MIN_M) __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -652,7 +663,7 @@ template <int M, int NR> __device__ __forceinline__ void zero(float (&acc)[NR][M
 // raw buffers of 1 + DEPTH items stay within the register budget.
 template <int T, int M, int NR> struct Depth {
     static constexpr int raw_dwords = (int)(sizeof(typename Tr<T>::Raw) / 4) * NR;
-    static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= 120) ? 2 : 1;
+    static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= REX_DEPTH_BUDGET) ? 2 : 1;
 };
 
 // One step of the single-pass walk.  Items are (row group g, wave step s):
