@@ -118,8 +118,9 @@ def main():
 
     W = w.make_weights()
     x = w.make_x(8)
-    copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / wbytes)))
-    Wd = torch.empty((copies, wbytes), dtype=torch.uint8, device=dev)
+    stored = w.stored_weight_bytes
+    copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / stored)))
+    Wd = torch.empty((copies, stored), dtype=torch.uint8, device=dev)
     src = torch.from_numpy(W.ravel()).to(dev)
     for c in range(copies):
         Wd[c].copy_(src)
@@ -139,10 +140,18 @@ def main():
     wptrs = [Wd[c].data_ptr() for c in range(copies)]
     xp = xd.data_ptr()
     yptrs = {m: ybufs[m].data_ptr() for m in ms}
-    qfr.row_exact_mv(t, Wd[0], xd, ybufs[ms[0]], n, k, ms[0], batch, strides, stream=hs)  # checked path once
+    idd = torch.from_numpy(w.make_ids()).to(dev) if w.experts else None
+    if w.experts:  # checked path once
+        qfr.row_exact_mv_gather(t, Wd[0], w.experts, idd, xd, ybufs[ms[0]], n, k, ms[0], batch, strides, stream=hs)
+    else:
+        qfr.row_exact_mv(t, Wd[0], xd, ybufs[ms[0]], n, k, ms[0], batch, strides, stream=hs)
 
     def launch(i, m):
-        rc = lib.row_exact_mv(int(t), wptrs[i % copies], xp, yptrs[m], n, k, m, batch, sp, hs)
+        if w.experts:
+            rc = lib.row_exact_mv_gather(int(t), wptrs[i % copies], w.experts, idd.data_ptr(), xp, yptrs[m], n, k, m,
+                                         batch, sp, hs)
+        else:
+            rc = lib.row_exact_mv(int(t), wptrs[i % copies], xp, yptrs[m], n, k, m, batch, sp, hs)
         if rc:
             raise qfr.RowExactError(rc, qfr.row_exact_last_error())
 
@@ -294,6 +303,18 @@ def cpu_baseline(w, W, x, ms, seconds):
     xrs, xbs, _, _ = w.strides(8)
     rb = oracle.row_bytes(t, k)
     probe = max(1, min(n, 16))
+    if w.experts:  # gathered product: whole calls
+        ids = w.make_ids()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < seconds:
+            for m in ms:
+                oracle.matvec_gather(t, W, w.experts, ids, x.ravel(), n, k, m, batch, xrs, xbs)
+            reps += 1
+        el = time.perf_counter() - t0
+        return {"value": round(rb * n * batch * len(ms) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                "kind": "oracle", "sample": f"{w.name}: {reps} whole step(s) at m={list(ms)}, float64 "
+                                            f"dequantize-then-dot, single thread, {el:.1f} s", "seconds": round(el, 2)}
     t0 = time.perf_counter()
     for m in ms:
         oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, probe))
@@ -328,9 +349,17 @@ def sweep(path, steps):
         xrs, xbs, yrs, ybs = w.strides(8)
         s = qfr.Strides(xrs, xbs, yrs, ybs)
         W = w.make_weights()
-        copies = max(2, int(np.ceil((1 << 30) / w.weight_bytes)))
+        copies = max(2, int(np.ceil((1 << 30) / w.stored_weight_bytes)))
         Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
         xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        idd = torch.from_numpy(w.make_ids()).cuda() if w.experts else None
+
+        def mv(i, y, m):
+            if w.experts:
+                qfr.row_exact_mv_gather(t, Wd[i % copies], w.experts, idd, xd, y, n, k, m, batch, s)
+            else:
+                qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
+
         rbytes = w.weight_bytes // 16 * 16
         reps = min(steps, 200)
 
@@ -354,8 +383,8 @@ def sweep(path, steps):
             _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, s)
             y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
             for i in range(10):
-                qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
-            us = span_us(lambda i: qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s))
+                mv(i, y, m)
+            us = span_us(lambda i: mv(i, y, m))
             sch = qfr.row_exact_schedule(t, n, k, m, batch)
             fl = 2.0 * n * k * m * batch
             res.append({"workload": w.name, "m": m, "kernel_us": round(us, 3),

@@ -149,6 +149,30 @@ int row_exact_mv_scheduled(row_exact_weight_t wt, const void *W, const float *x,
                            uint32_t k, uint32_t m, uint32_t batch, const row_exact_strides_t *strides,
                            const row_exact_schedule_t *schedule, hipStream_t stream);
 
+/* Gathered product for mixture-of-experts layers: batch entry b multiplies
+ * by weight set expert_ids[b] of num_experts sets instead of set b,
+ *   y[b, j, :] = W[expert_ids[b]] . x[b, j, :],
+ * the per-expert weight selection of nuvec-core 0.6.0, src/gpu.rs (the
+ * GatherQmm / GatherMm fast ops; tokens grouped by expert as its
+ * SortedOffsets primitive groups them), here over the row-exact block types
+ * and with the row-exact contract: every output has the bits row_exact_mv
+ * gives for that batch entry with W advanced to its weight set.
+ *  W          : device pointer to num_experts * n rows of
+ *               row_exact_row_bytes(wt, k) bytes; set e starts at
+ *               e * n * row_bytes.
+ *  expert_ids : device int32[batch], 4-byte aligned, caller-owned, only read
+ *               (by the kernel, so it may be written by earlier work on the
+ *               same stream).  An id outside [0, num_experts) reads no
+ *               weights and sets that batch entry's m*n outputs to NaN.
+ *  x, y, n, k, m, batch, strides, stream : as row_exact_mv (a token routed
+ *               to several experts can use x_batch_stride = 0).
+ * Errors: as row_exact_mv, plus ROW_EXACT_EARG for NULL expert_ids or
+ * num_experts == 0, ROW_EXACT_EALIGN for misaligned expert_ids, and
+ * ROW_EXACT_EALIAS if y overlaps expert_ids[0 .. batch). */
+int row_exact_mv_gather(row_exact_weight_t wt, const void *W, uint32_t num_experts, const int32_t *expert_ids,
+                        const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                        const row_exact_strides_t *strides, hipStream_t stream);
+
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
  * depends on (wt, k) only; the packing fields may depend on every argument
  * and on the current device.  Writes *out; errors: EARG, EHIP. */

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
         lib.oracle_dequant.argtypes = [ctypes.c_int, P, u32, u32, P]
         lib.oracle_matvec_rows.restype = ctypes.c_int
         lib.oracle_matvec_rows.argtypes = [ctypes.c_int, P, P, u32, u32, u32, u32, u32, u32, u32, u32, P, P]
+        lib.oracle_matvec_gather.restype = ctypes.c_int
+        lib.oracle_matvec_gather.argtypes = [ctypes.c_int, P, u32, P, P, u32, u32, u32, u32, u32, u32, P, P]
         _lib = lib
     return _lib
 
@@ -146,4 +148,27 @@ def matvec(wtype: int, W: np.ndarray, x: np.ndarray, n: int, k: int, m: int, bat
                                 _ptr(y), _ptr(a))
     if rc != 0:
         raise ValueError(f"oracle_matvec_rows failed ({rc})")
+    return y, a
+
+
+def matvec_gather(wtype: int, W: np.ndarray, num_experts: int, ids: np.ndarray, x: np.ndarray, n: int, k: int,
+                  m: int, batch: int, x_row_stride: Optional[int] = None,
+                  x_batch_stride: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Float64 reference ``(y, a)`` of the gathered product, each ``[batch, m, n]``:
+    batch entry ``b`` uses weight set ``ids[b]``; ids outside the sets give NaN."""
+    lib = _load()
+    xrs = k if x_row_stride is None else x_row_stride
+    Wb = np.ascontiguousarray(W, dtype=np.uint8).ravel()
+    ib = np.ascontiguousarray(ids, dtype=np.int32).ravel()
+    xf = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    if Wb.size < row_bytes(wtype, k) * n * num_experts or ib.size < batch:
+        raise ValueError("oracle.matvec_gather: buffers too small")
+    if xf.size < (batch - 1) * x_batch_stride + (m - 1) * xrs + k:
+        raise ValueError("oracle.matvec_gather: input too small")
+    y = np.empty((batch, m, n), dtype=np.float64)
+    a = np.empty((batch, m, n), dtype=np.float64)
+    rc = lib.oracle_matvec_gather(wtype, _ptr(Wb), num_experts, _ptr(ib), _ptr(xf), n, k, m, batch, xrs,
+                                  x_batch_stride, _ptr(y), _ptr(a))
+    if rc != 0:
+        raise ValueError(f"oracle_matvec_gather failed ({rc})")
     return y, a

@@ -266,3 +266,29 @@ int oracle_matvec(int type, const uint8_t *W, const float *x, uint32_t n, uint32
                   uint32_t batch, uint32_t xrs, uint32_t xbs, double *y, double *a) {
     return oracle_matvec_rows(type, W, x, n, k, m, batch, xrs, xbs, 0, n, y, a);
 }
+
+/* Gathered product (per-expert weight selection: nuvec-core 0.6.0,
+ * src/gpu.rs, GatherQmm / GatherMm).  As oracle_matvec_rows, except that
+ * batch entry b takes its weight rows from set ids[b] of num_experts sets
+ * (set e at byte e * n * row_bytes); an id outside [0, num_experts) gives NaN
+ * for all of that entry's outputs (and its absolute sums). */
+int oracle_matvec_gather(int type, const uint8_t *W, uint32_t num_experts, const int32_t *ids, const float *x,
+                         uint32_t n, uint32_t k, uint32_t m, uint32_t batch, uint32_t xrs, uint32_t xbs,
+                         double *y, double *a) {
+    if (!k_ok(type, k) || m == 0 || n == 0 || batch == 0 || num_experts == 0) return -1;
+    uint64_t rb = oracle_row_bytes(type, k);
+    for (uint32_t b = 0; b < batch; ++b) {
+        size_t o = (size_t)b * m * n;
+        if (ids[b] < 0 || (uint32_t)ids[b] >= num_experts) {
+            for (size_t q = 0; q < (size_t)m * n; ++q) {
+                y[o + q] = NAN;
+                a[o + q] = NAN;
+            }
+            continue;
+        }
+        const uint8_t *We = W + rb * (uint64_t)n * (uint32_t)ids[b];
+        int rc = oracle_matvec_rows(type, We, x + (uint64_t)b * xbs, n, k, m, 1, xrs, 0, 0, n, y + o, a + o);
+        if (rc) return rc;
+    }
+    return 0;
+}

@@ -18,7 +18,7 @@ from typing import Any, Optional, Tuple
 __all__ = [
     "Weight", "Strides", "Schedule", "RowExactError", "LibraryMissing", "MAX_ROWS",
     "contiguous", "grouped_token_major", "library_path", "load_library",
-    "row_exact_mv", "row_exact_mv_scheduled", "row_exact_schedule", "row_exact_row_bytes",
+    "row_exact_mv", "row_exact_mv_scheduled", "row_exact_mv_gather", "row_exact_schedule", "row_exact_row_bytes",
     "row_exact_required_bytes", "row_exact_dequant", "row_exact_last_error", "row_exact_launch_count",
     "row_exact_stream_read", "row_exact_stream_read_shapes",
 ]
@@ -112,6 +112,8 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_mv.argtypes = [ctypes.c_int, P, P, P, u32, u32, u32, u32, SP, P]
     lib.row_exact_mv_scheduled.restype = ctypes.c_int
     lib.row_exact_mv_scheduled.argtypes = [ctypes.c_int, P, P, P, u32, u32, u32, u32, SP, SchP, P]
+    lib.row_exact_mv_gather.restype = ctypes.c_int
+    lib.row_exact_mv_gather.argtypes = [ctypes.c_int, P, u32, P, P, P, u32, u32, u32, u32, SP, P]
     lib.row_exact_schedule.restype = ctypes.c_int
     lib.row_exact_schedule.argtypes = [ctypes.c_int, u32, u32, u32, u32, SchP]
     lib.row_exact_row_bytes.restype = u64
@@ -205,6 +207,30 @@ def row_exact_mv_scheduled(wt: int, W: Any, x: Any, y: Any, n: int, k: int, m: i
     sp = ctypes.byref(strides) if strides is not None else None
     _check(lib.row_exact_mv_scheduled(int(wt), wp, xp, yp, n, k, m, batch, sp, ctypes.byref(schedule),
                                       _stream_handle(stream)))
+
+
+def row_exact_mv_gather(wt: int, W: Any, num_experts: int, expert_ids: Any, x: Any, y: Any, n: int, k: int,
+                        m: int, batch: int, strides: Optional[Strides] = None, stream: Any = None) -> None:
+    """Enqueue ``y[b, j, :] = W[expert_ids[b]] . x[b, j, :]`` (see ``row_exact_mv_gather``)."""
+    wt = Weight(wt)
+    lib = load_library()
+    _dtype_check(wt, W, x, y)
+    _, xb, yb = row_exact_required_bytes(wt, n, k, m, batch, strides)
+    wb = row_exact_row_bytes(wt, k) * n * num_experts
+    for t, need, name in ((W, wb, "weight"), (x, xb, "input"), (y, yb, "output"), (expert_ids, 4 * batch, "expert_ids")):
+        _, have = _ptr_and_bytes(t, name)
+        if have is not None and have < need:
+            raise ValueError(f"{name} holds {have} bytes, needs {need}")
+    if not isinstance(expert_ids, int):
+        import torch
+        if expert_ids.dtype != torch.int32:
+            raise ValueError(f"expert_ids must be int32, got {expert_ids.dtype}")
+    wp, _ = _ptr_and_bytes(W, "weight")
+    ip, _ = _ptr_and_bytes(expert_ids, "expert_ids")
+    xp, _ = _ptr_and_bytes(x, "input")
+    yp, _ = _ptr_and_bytes(y, "output")
+    sp = ctypes.byref(strides) if strides is not None else None
+    _check(lib.row_exact_mv_gather(int(wt), wp, num_experts, ip, xp, yp, n, k, m, batch, sp, _stream_handle(stream)))
 
 
 def row_exact_schedule(wt: int, n: int, k: int, m: int, batch: int = 1) -> Schedule:

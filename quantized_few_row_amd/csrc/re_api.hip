@@ -147,9 +147,10 @@ int check_shape(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch) {
     return 0;
 }
 
+// Byte extents of W (weight_sets sets of n rows), x and y.
 int sizes(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, const row_exact_strides_t &s, uint64_t &wb,
-          uint64_t &xb, uint64_t &yb) {
-    const u128 w = (u128)row_bytes_of(t, k) * n * batch;
+          uint64_t &xb, uint64_t &yb, uint32_t weight_sets = 0) {
+    const u128 w = (u128)row_bytes_of(t, k) * n * (weight_sets ? weight_sets : batch);
     const u128 x = extent(batch, s.x_batch_stride, m, s.x_row_stride, k) * 4;
     const u128 y = extent(batch, s.y_batch_stride, m, s.y_row_stride, n) * 4;
     const u128 lim = (u128)1 << 62;
@@ -164,10 +165,13 @@ int sizes(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, const row_e
 bool overlap(uintptr_t a, uint64_t an, uintptr_t b, uint64_t bn) { return a < b + bn && b < a + an; }
 
 int validate_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
-                const row_exact_strides_t &s, uint64_t &wb, uint64_t &xbytes, uint64_t &ybytes) {
+                const row_exact_strides_t &s, uint64_t &wb, uint64_t &xbytes, uint64_t &ybytes,
+                const int32_t *ids = nullptr, uint32_t num_experts = 0) {
     int rc = check_shape(t, n, k, m, batch);
     if (rc) return rc;
     if (!W || !x || !y) return fail(ROW_EXACT_EARG, "W, x and y must be non-NULL device pointers");
+    if (ids && num_experts == 0) return fail(ROW_EXACT_EARG, "num_experts must be > 0");
+    if (ids && (uintptr_t)ids % 4) return fail(ROW_EXACT_EALIGN, "expert_ids must be 4-byte aligned");
     if (s.x_row_stride % 4 || s.x_batch_stride % 4 || ((uintptr_t)x % 16))
         return fail(s.x_row_stride % 4 || s.x_batch_stride % 4 ? ROW_EXACT_ESTRIDE : ROW_EXACT_EALIGN,
                     "input strides (%u, %u) must be multiples of 4 and the input pointer 16-byte aligned "
@@ -191,13 +195,14 @@ int validate_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint
     if (!ok)
         return fail(ROW_EXACT_EALIAS, "output strides overlap: y_row_stride %u, y_batch_stride %u, m %u, n %u, batch %u",
                     s.y_row_stride, s.y_batch_stride, m, n, batch);
-    rc = sizes(t, n, k, m, batch, s, wb, xbytes, ybytes);
+    rc = sizes(t, n, k, m, batch, s, wb, xbytes, ybytes, ids ? num_experts : 0);
     if (rc) return rc;
     if (row_bytes_of(t, k) > 0x7fffffffull)
         return fail(ROW_EXACT_EEXTENT, "a weight row of %llu bytes exceeds 2^31 - 1",
                     (unsigned long long)row_bytes_of(t, k));
-    if (overlap((uintptr_t)y, ybytes, (uintptr_t)W, wb) || overlap((uintptr_t)y, ybytes, (uintptr_t)x, xbytes))
-        return fail(ROW_EXACT_EALIAS, "output range overlaps the weight or input range");
+    if (overlap((uintptr_t)y, ybytes, (uintptr_t)W, wb) || overlap((uintptr_t)y, ybytes, (uintptr_t)x, xbytes) ||
+        (ids && overlap((uintptr_t)y, ybytes, (uintptr_t)ids, 4ull * batch)))
+        return fail(ROW_EXACT_EALIAS, "output range overlaps the weight, input or expert-id range");
     return 0;
 }
 
@@ -266,9 +271,11 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         // balances the tail across workgroups), one row group per wave while
         // the rows allow it, single rows beyond that.
         const uint64_t target = (uint64_t)di.cus * 32;
-        const uint32_t nr = (rows > target && rows <= 2 * target) ? 2u : 1u;
+        const uint64_t wave_rows = rows >> (6 - lanes_per_row_log2(t, k));  // rows / slots per wave
+        const uint32_t nr = (wave_rows > target && wave_rows <= 2 * target) ? 2u : 1u;
         s.rows_per_wave = nr;
-        const uint32_t gpb = (n + nr - 1) / nr;
+        const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
+        const uint32_t gpb = (n + rg - 1) / rg;
         uint32_t waves = 8;
         while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
         s.waves_per_workgroup = waves;
@@ -281,9 +288,10 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     // rows per wave: the most that still leaves 8 waves per CU
     const uint64_t target_waves = (uint64_t)di.cus * 8;
     uint32_t nr = max_rows_per_wave(t, m);
-    while (nr > 1 && rows / nr < target_waves) nr >>= 1;
+    while (nr > 1 && (rows >> (6 - lanes_per_row_log2(t, k))) / nr < target_waves) nr >>= 1;
     s.rows_per_wave = nr;
-    const uint32_t gpb = (n + nr - 1) / nr;
+    const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
+    const uint32_t gpb = (n + rg - 1) / rg;
     uint32_t waves = 8;
     while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
     s.waves_per_workgroup = waves;
@@ -357,11 +365,12 @@ DqLauncher dq_launcher(int t) {
 }
 
 int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
-        const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream) {
+        const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream,
+        const int32_t *ids = nullptr, uint32_t num_experts = 0) {
     g_err.clear();
     const row_exact_strides_t s = resolve_strides(strides, m, n, k);
     uint64_t wb, xbytes, ybytes;
-    int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes);
+    int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes, ids, num_experts);
     if (rc) return rc;
     if (pin) {
         rc = check_schedule_fields(t, k, *pin);
@@ -394,8 +403,10 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     a.xrs = s.x_row_stride;
     a.yrs = s.y_row_stride;
     a.pieces = pieces_of(t, k);
+    a.lpr_log2 = lanes_per_row_log2(t, k);
     const uint32_t nr = sch.rows_per_wave;
-    a.groups_per_batch = (n + nr - 1) / nr;
+    const uint32_t rg = nr << (6 - a.lpr_log2);  // rows per group: NR rows in each of the wave's slots
+    a.groups_per_batch = (n + rg - 1) / rg;
     uint32_t wgs = sch.workgroups_per_batch < a.groups_per_batch ? sch.workgroups_per_batch : a.groups_per_batch;
     a.groups_per_wg = (a.groups_per_batch + wgs - 1) / wgs;
     wgs = (a.groups_per_batch + a.groups_per_wg - 1) / a.groups_per_wg;  // as the kernel recomputes it
@@ -410,6 +421,8 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
         a.nchunks = (a.pieces + a.pieces_per_chunk - 1) / a.pieces_per_chunk;
     }
     a.xs_stride = xs_stride(t, a.kchunk);
+    a.ids = ids;
+    a.num_experts = num_experts;
     const uint64_t grid_x = (uint64_t)wgs * batch;
     if (grid_x > 0x7fffffffull)
         return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);
@@ -437,6 +450,16 @@ int row_exact_mv_scheduled(row_exact_weight_t wt, const void *W, const float *x,
         return fail(ROW_EXACT_ESCHEDULE, "schedule must be non-NULL");
     }
     return run((int)wt, W, x, y, n, k, m, batch, strides, schedule, stream);
+}
+
+int row_exact_mv_gather(row_exact_weight_t wt, const void *W, uint32_t num_experts, const int32_t *expert_ids,
+                        const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                        const row_exact_strides_t *strides, hipStream_t stream) {
+    if (!expert_ids) {
+        g_err.clear();
+        return fail(ROW_EXACT_EARG, "expert_ids must be a non-NULL device pointer");
+    }
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, expert_ids, num_experts);
 }
 
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,

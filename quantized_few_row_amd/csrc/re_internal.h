@@ -26,6 +26,9 @@ struct MvArgs {
     uint32_t pieces_per_chunk;  // multiple of 64 (one wave step)
     uint32_t kchunk;            // values per pass
     uint32_t xs_stride;         // floats per staged x row in LDS (padded)
+    uint32_t lpr_log2;          // log2 of the lanes per weight row (6, or 5 / 4 for short rows)
+    const int32_t *ids;         // per-batch weight selection (NULL: batch b uses weights b)
+    uint32_t num_experts;       // number of weight sets ids may select
 };
 
 struct DqArgs {
@@ -88,6 +91,13 @@ inline uint32_t pieces_of(int t, uint32_t k) {
     case kBF16: return Geo<kBF16>::pieces(k);
     default: return Geo<kQ5_0>::pieces(k);
     }
+}
+// Lanes that split one weight row, a function of (type, k) only: 64, or 32 /
+// 16 when a row has at most 32 / 16 pieces (a wave then covers 2 / 4 rows at
+// once instead of leaving lanes idle).
+inline uint32_t lanes_per_row_log2(int t, uint32_t k) {
+    const uint32_t p = pieces_of(t, k);
+    return p <= 16 ? 4u : p <= 32 ? 5u : 6u;
 }
 inline uint32_t pad_period(int t) {
     switch (t) {

@@ -434,62 +434,89 @@ constexpr int pow2ceil(int v) { return v <= 1 ? 1 : 2 * pow2ceil((v + 1) / 2); }
 
 // Sum each of the NR*M accumulators over the 64 lanes with the fixed tree
 // and store output (r, j) to y[j*yrs + row0 + r] when row0 + r < n.
-template <int M, int NR>
+template <int M, int NR, int L>
 __device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *__restrict__ yb, uint32_t yrs,
                                              uint32_t n, uint32_t row0, uint32_t lane) {
+    // L lanes per weight row: slot lane / L of the wave holds rows
+    // row0 + slot*NR + r.  The tree over a slot's lanes is the last log2(L)
+    // levels of the 64-lane tree.
     constexpr int NA = NR * M;
     constexpr int A = pow2ceil(NA);
     float v[A];
 #pragma unroll
     for (int a = 0; a < A; ++a) v[a] = a < NA ? acc[a / M][a % M] : 0.0f;
 
-    // level 1: (L, L^32)
-    constexpr int A1 = A >= 2 ? A / 2 : 1;
-    if constexpr (A >= 2) {
+    // level 1: (L, L^32), 64-lane rows only
+    constexpr int A1 = L < 64 ? A : (A >= 2 ? A / 2 : 1);
+    if constexpr (L == 64) {
+        if constexpr (A >= 2) {
 #pragma unroll
-        for (int a = 0; a < A1; ++a) v[a] = swap32_add(v[a], v[a + A1]);
-    } else {
-        v[0] = swap32_add(v[0], v[0]);
+            for (int a = 0; a < A1; ++a) v[a] = swap32_add(v[a], v[a + A1]);
+        } else {
+            v[0] = swap32_add(v[0], v[0]);
+        }
     }
-    // level 2: (L, L^16)
-    constexpr int A2 = A1 >= 2 ? A1 / 2 : 1;
-    if constexpr (A1 >= 2) {
+    // level 2: (L, L^16), 64- and 32-lane rows
+    constexpr int A2 = L < 32 ? A1 : (A1 >= 2 ? A1 / 2 : 1);
+    if constexpr (L >= 32) {
+        if constexpr (A1 >= 2) {
 #pragma unroll
-        for (int a = 0; a < A2; ++a) v[a] = swap16_add(v[a], v[a + A2]);
-    } else {
-        v[0] = swap16_add(v[0], v[0]);
+            for (int a = 0; a < A2; ++a) v[a] = swap16_add(v[a], v[a + A2]);
+        } else {
+            v[0] = swap16_add(v[0], v[0]);
+        }
     }
     // levels 3..6 inside each row of 16 lanes
+    constexpr int AN = L < 32 ? NA : A2;
 #pragma unroll
-    for (int a = 0; a < A2; ++a) {
+    for (int a = 0; a < AN; ++a) {
         v[a] = v[a] + dpp_mov<0x128>(v[a]);  // row_ror:8     (L, L^8)
         v[a] = v[a] + dpp_mov<0x141>(v[a]);  // row_half_mirror (L, 7-L)
         v[a] = v[a] + dpp_mov<0x4E>(v[a]);   // quad_perm 2,3,0,1
         v[a] = v[a] + dpp_mov<0xB1>(v[a]);   // quad_perm 1,0,3,2
     }
 
-    // Which lanes hold which outputs: A >= 4: row R = lane/16 holds outputs
-    // R*A2 + a; A == 2: lanes 0..31 output 0, lanes 32..63 output 1; A == 1:
-    // every lane output 0.
-    uint32_t base;
+    // Which lanes hold which outputs of their slot.  L == 64: A >= 4: row
+    // R = lane/16 holds outputs R*A2 + a; A == 2: lanes 0..31 output 0,
+    // lanes 32..63 output 1; A == 1: lane 0.  L == 32: A >= 2: the 16-lane
+    // row R of the slot holds outputs R*A2 + a; A == 1: the slot's first lane.
+    // L == 16: the row's first lane holds all outputs.
+    uint32_t base, slot;
     bool holder;
-    if constexpr (A >= 4) {
-        holder = (lane & 15) == 0;
-        base = (lane >> 4) * A2;
-    } else if constexpr (A == 2) {
-        holder = (lane & 31) == 0;
-        base = lane >> 5;
+    if constexpr (L == 64) {
+        slot = 0;
+        if constexpr (A >= 4) {
+            holder = (lane & 15) == 0;
+            base = (lane >> 4) * A2;
+        } else if constexpr (A == 2) {
+            holder = (lane & 31) == 0;
+            base = lane >> 5;
+        } else {
+            holder = lane == 0;
+            base = 0;
+        }
+    } else if constexpr (L == 32) {
+        slot = lane >> 5;
+        if constexpr (A >= 2) {
+            holder = (lane & 15) == 0;
+            base = ((lane >> 4) & 1) * A2;
+        } else {
+            holder = (lane & 31) == 0;
+            base = 0;
+        }
     } else {
-        holder = lane == 0;
+        slot = lane >> 4;
+        holder = (lane & 15) == 0;
         base = 0;
     }
     if (holder) {
 #pragma unroll
-        for (int a = 0; a < A2; ++a) {
+        for (int a = 0; a < AN; ++a) {
             const uint32_t o = base + a;
             if (o < (uint32_t)NA) {
                 const uint32_t r = o / M, j = o % M;
-                if (row0 + r < n) yb[(uint64_t)j * yrs + row0 + r] = v[a];
+                const uint32_t row = row0 + slot * NR + r;
+                if (row < n) yb[(uint64_t)j * yrs + row] = v[a];
             }
         }
     }
@@ -628,10 +655,14 @@ __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *c
     }
 }
 
-// Wave-uniform base (aligned down to 4 bytes) and byte offset of each row.
+// Wave-uniform base (aligned down to 4 bytes) and per-lane byte offset of
+// each of a lane's rows: row0 + r for the wave's first slot, plus slot_rows
+// for the lane's slot (short rows; slot_rows = 0 with 64 lanes per row).
+// Rows past n are clamped to n - 1 (read, never stored).
 template <int NR>
 __device__ __forceinline__ void row_bases(const uint8_t *Wb, uint64_t row_bytes, uint32_t n, uint32_t row0,
-                                          const uint8_t *(&R)[NR], uint32_t (&o0)[NR]) {
+                                          bool sub_wave, uint32_t slot_rows, const uint8_t *(&R)[NR],
+                                          uint32_t (&o0)[NR]) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const uint32_t row = min(row0 + r, n - 1);
@@ -639,17 +670,35 @@ __device__ __forceinline__ void row_bases(const uint8_t *Wb, uint64_t row_bytes,
         const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
         R[r] = rp - lo;
         o0[r] = lo;
+        if (sub_wave) o0[r] += (uint32_t)((min(row0 + slot_rows + r, n - 1) - row) * row_bytes);
     }
 }
 
-template <int T, int NR>
+// log2 of the lanes per row: 6 for the 64-lane instances, a.lpr_log2 (5 or
+// 4) for the short-row instances.
+template <bool SUB> __device__ __forceinline__ uint32_t lpr_of(const MvArgs &a) { return SUB ? a.lpr_log2 : 6u; }
+
+template <int T, int NR, bool SUB>
 __device__ __forceinline__ void load_item(const uint8_t *Wb, const MvArgs &a, uint32_t g, uint32_t p,
-                                          typename Tr<T>::Raw (&raw)[NR]) {
+                                          uint32_t slot, typename Tr<T>::Raw (&raw)[NR]) {
     const uint8_t *R[NR];
     uint32_t o0[NR];
-    row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
+    row_bases<NR>(Wb, a.row_bytes, a.n, (g * NR) << (6 - lpr_of<SUB>(a)), SUB, slot * NR, R, o0);
 #pragma unroll
     for (int r = 0; r < NR; ++r) raw[r] = Tr<T>::load(R[r], o0[r], p, a.k);
+}
+
+// The group's outputs, with the tree for the lanes-per-row of this k.
+template <int M, int NR, bool SUB>
+__device__ __forceinline__ void store_group(const MvArgs &a, const float (&acc)[NR][M], float *__restrict__ yb,
+                                            uint32_t g, uint32_t lane) {
+    const uint32_t row0 = (g * NR) << (6 - lpr_of<SUB>(a));
+    if constexpr (!SUB)
+        reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, row0, lane);
+    else if (a.lpr_log2 == 5)
+        reduce_store<M, NR, 32>(acc, yb, a.yrs, a.n, row0, lane);
+    else
+        reduce_store<M, NR, 16>(acc, yb, a.yrs, a.n, row0, lane);
 }
 
 template <int M, int NR> __device__ __forceinline__ void zero(float (&acc)[NR][M]) {
@@ -666,28 +715,30 @@ template <int T, int M, int NR> struct Depth {
     static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= REX_DEPTH_BUDGET) ? 2 : 1;
 };
 
-// One step of the single-pass walk.  Items are (row group g, wave step s):
-// pieces 64s + lane of the group's NR rows.  The load cursor (lg, ls) runs
+// One step of the single-pass walk.  Items are (row group g, step s):
+// pieces L*s + li of the group's rows, for the lane's index li < L in its
+// row slot (L lanes per row; L = 64: one slot of NR rows).  The load cursor (lg, ls) runs
 // DEPTH items ahead of the compute cursor (cg, cs): the step loads the item
 // at the load cursor into `nxt`, multiplies `cur`, and stores a group's
 // outputs after its last step.  Returns whether items remain.
-template <int T, int M, int NR>
+template <int T, int M, int NR, bool SUB>
 __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__restrict__ Wb, float *__restrict__ yb,
                                           const float *__restrict__ xs, uint32_t XS, uint32_t &lg, uint32_t &ls,
                                           uint32_t &cg, uint32_t &cs, uint32_t gstride, uint32_t g1, uint32_t S,
-                                          uint32_t lane, const typename Tr<T>::Raw (&cur)[NR],
-                                          typename Tr<T>::Raw (&nxt)[NR], float (&acc)[NR][M]) {
+                                          uint32_t lane, uint32_t li, uint32_t slot,
+                                          const typename Tr<T>::Raw (&cur)[NR], typename Tr<T>::Raw (&nxt)[NR],
+                                          float (&acc)[NR][M]) {
     if (lg < g1) {
-        load_item<T, NR>(Wb, a, lg, min(ls * 64 + lane, a.pieces - 1), nxt);
+        load_item<T, NR, SUB>(Wb, a, lg, min((ls << lpr_of<SUB>(a)) + li, a.pieces - 1), slot, nxt);
         if (++ls == S) {
             ls = 0;
             lg += gstride;
         }
     }
-    const uint32_t pc = cs * 64 + lane;
+    const uint32_t pc = (cs << lpr_of<SUB>(a)) + li;
     if (pc < a.pieces) compute_piece<T, M, NR>(acc, cur, pc, 0, xs, XS, a.k);
     if (cs == S - 1) {
-        reduce_store<M, NR>(acc, yb, a.yrs, a.n, cg * NR, lane);
+        store_group<M, NR, SUB>(a, acc, yb, cg, lane);
         zero<M, NR>(acc);
     }
     if (++cs == S) {
@@ -699,7 +750,9 @@ __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__rest
 
 // ---------------------------------------------------------------- kernels
 
-template <int T, int M, int NR>
+// SUB: instances for short rows (32 or 16 lanes per row, a.lpr_log2 5 / 4);
+// the others have 64 lanes per row as compile-time constants.
+template <int T, int M, int NR, bool SUB>
 __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     extern __shared__ float xs[];
     const uint32_t lane = threadIdx.x & 63u;
@@ -709,10 +762,25 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     const uint32_t b = blockIdx.x / wgs_per_batch;  // batch-major flattening
     const uint32_t w = blockIdx.x - b * wgs_per_batch;
     const float *__restrict__ xb = a.x + b * a.xbs;
-    const uint8_t *__restrict__ Wb = a.W + b * a.batch_bytes;
     float *__restrict__ yb = a.y + b * a.ybs;
     const uint32_t g0 = w * a.groups_per_wg;
     const uint32_t g1 = min(g0 + a.groups_per_wg, a.groups_per_batch);
+    // Weight set of this batch entry: b, or ids[b] for a gathered product.
+    // An id outside [0, num_experts) reads nothing and yields NaN outputs.
+    uint64_t wsel = b;
+    if (a.ids) {
+        const int32_t e = a.ids[b];
+        if (e < 0 || (uint32_t)e >= a.num_experts) {
+            const uint32_t r1 = min((g1 * NR) << (6 - lpr_of<SUB>(a)), a.n);
+            for (uint32_t row = ((g0 * NR) << (6 - lpr_of<SUB>(a))) + threadIdx.x; row < r1; row += blockDim.x) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) yb[(uint64_t)j * a.yrs + row] = __builtin_nanf("");
+            }
+            return;
+        }
+        wsel = (uint32_t)e;
+    }
+    const uint8_t *__restrict__ Wb = a.W + wsel * a.batch_bytes;
     const uint32_t XS = a.xs_stride;
 
     if (a.nchunks == 1) {
@@ -721,19 +789,21 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         // flight.  The first DEPTH items are requested before x is staged.
         using Raw = typename Tr<T>::Raw;
         constexpr int DEPTH = Depth<T, M, NR>::value;
-        const uint32_t S = (a.pieces + 63) >> 6;
+        const uint32_t lpr = lpr_of<SUB>(a);
+        const uint32_t li = lane & ((1u << lpr) - 1), slot = lane >> lpr;
+        const uint32_t S = (a.pieces + (1u << lpr) - 1) >> lpr;
         uint32_t lg = g0 + wave, ls = 0;
         const uint32_t gfirst = lg;
         Raw A[NR], B[NR], C[NR];
         if (lg < g1) {
-            load_item<T, NR>(Wb, a, lg, min(lane, a.pieces - 1), A);
+            load_item<T, NR, SUB>(Wb, a, lg, min(li, a.pieces - 1), slot, A);
             if (++ls == S) {
                 ls = 0;
                 lg += nwaves;
             }
         }
         if (DEPTH == 2 && lg < g1) {
-            load_item<T, NR>(Wb, a, lg, min(ls * 64 + lane, a.pieces - 1), B);
+            load_item<T, NR, SUB>(Wb, a, lg, min((ls << lpr) + li, a.pieces - 1), slot, B);
             if (++ls == S) {
                 ls = 0;
                 lg += nwaves;
@@ -746,19 +816,20 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             zero<M, NR>(acc);
             uint32_t cg = gfirst, cs = 0;
             if constexpr (DEPTH == 2) {
-                while (walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, A, C, acc) &&
-                       walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, B, A, acc) &&
-                       walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, C, B, acc)) {
+                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, A, C, acc) &&
+                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, B, A, acc) &&
+                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, C, B, acc)) {
                 }
             } else {
-                while (walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, A, B, acc) &&
-                       walk_step<T, M, NR>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, B, A, acc)) {
+                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, A, B, acc) &&
+                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, B, A, acc)) {
                 }
             }
         }
-    } else {
-        // Several LDS passes over K: every wave of the workgroup works on one
-        // row group per round and all waves stage each pass together.
+    } else if constexpr (!SUB) {
+        // Several LDS passes over K (only for rows of more than 64 pieces, so
+        // 64 lanes per row): every wave of the workgroup works on one row
+        // group per round and all waves stage each pass together.
         for (uint32_t base = g0; base < g1; base += nwaves) {
             const uint32_t g = base + wave;
             const bool active = g < g1;
@@ -766,7 +837,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             zero<M, NR>(acc);
             const uint8_t *R[NR];
             uint32_t o0[NR];
-            row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, R, o0);
+            row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, false, 0, R, o0);
             for (uint32_t c = 0; c < a.nchunks; ++c) {
                 const uint32_t pb = c * a.pieces_per_chunk;
                 const uint32_t pe = min(pb + a.pieces_per_chunk, a.pieces);
@@ -777,7 +848,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 __syncthreads();
                 if (active) accumulate<T, M, NR>(acc, R, o0, pb, pe, vb, xs, XS, a.k, lane);
             }
-            if (active) reduce_store<M, NR>(acc, yb, a.yrs, a.n, g * NR, lane);
+            if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane);
         }
     }
 }
@@ -809,7 +880,7 @@ __global__ void __launch_bounds__(256) dq_kernel(const DqArgs a) {
 
 template <int T, int M, int NR>
 hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    const void *fn = (const void *)mv_kernel<T, M, NR>;
+    const void *fn = a.lpr_log2 < 6 ? (const void *)mv_kernel<T, M, NR, true> : (const void *)mv_kernel<T, M, NR, false>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -821,7 +892,7 @@ hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStr
 
 template <int T, int M, int NR>
 hipError_t attributes_one(hipFuncAttributes *attr) {
-    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR>);
+    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR, false>);
 }
 
 template <int T, int M>

@@ -36,7 +36,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = qfr.load_library()
     declared = _declared_functions()
-    assert len(declared) == 10, declared
+    assert len(declared) == 11, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -223,3 +223,35 @@ def test_stream_read_probe_rejects_bad_arguments():
         assert lib.row_exact_stream_read(*args, None) == code, args
         assert "stream_read" in qfr.row_exact_last_error()
     assert qfr.row_exact_launch_count() == before
+
+
+def _gather(ids=XP + 0x100000, num_experts=4, W=WP, x=XP, y=YP, n=64, k=256, m=2, batch=3, wt=Weight.Q8_0):
+    lib = qfr.load_library()
+    st = Strides(k, 0, batch * n, n)  # one token's x for every entry, token-major y
+    return lib.row_exact_mv_gather(int(wt), W, num_experts, ids, x, y, n, k, m, batch, ctypes.byref(st), None), \
+        qfr.row_exact_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(ids=0), -1, "expert_ids"),
+    (dict(num_experts=0), -1, "num_experts"),
+    (dict(ids=XP + 0x100002), -2, "4-byte aligned"),
+    (dict(ids=YP + 8), -4, "expert-id"),
+    (dict(m=0), -1, "m (0)"),
+    (dict(wt=9), -1, "unknown weight type"),
+])
+def test_gather_invalid_arguments(kw, code, text):
+    before = qfr.row_exact_launch_count()
+    rc, msg = _gather(**kw)
+    assert rc == code, (rc, msg)
+    assert text in msg, msg
+    assert qfr.row_exact_launch_count() == before
+
+
+def test_gather_weight_extent_counts_expert_sets():
+    # y placed just past W's 4 sets of 64 Q8_0 rows: no overlap with 4 sets,
+    # overlap when W holds 5 sets
+    rb = qfr.row_exact_row_bytes(Weight.Q8_0, 256)
+    y = WP + 4 * 64 * rb
+    rc, msg = _gather(num_experts=5, y=y, ids=XP + 0x100000)
+    assert rc == -4 and "overlaps" in msg

@@ -177,3 +177,31 @@ def test_default_schedule_properties():
             assert splits == {1}
             s = qfr.row_exact_schedule(t, 4096, k, 8)
             assert s.rows_per_wave in (1, 2, 4) and 1 <= s.waves_per_workgroup <= 8
+
+
+# Short rows: a row of at most 16 / 32 pieces is split by 16 / 32 lanes and a
+# wave covers 4 / 2 rows at once (the lane map is a function of (type, k)).
+SHORT_K = {wl.F16: (124, 252), wl.Q8_0: (512, 1024), wl.Q4_K: (1024, 2048), wl.Q6_K: (1024, 2048),
+           wl.Q5_0: (480, 1024), wl.F32: (64, 100), wl.BF16: (60, 256)}
+SHORT = [(t, k) for t in TYPES for k in SHORT_K[t]]
+
+
+@pytest.mark.parametrize("t,k", SHORT, ids=[f"{wl.TYPE_NAMES[t]}-k{k}" for t, k in SHORT])
+def test_short_rows_lane_maps(t, k):
+    n = 67
+    W = wl.weights(t, n, k, seed=950 + t)
+    x = wl.activations(8, k, seed=960 + t)
+    Wd, xd = to_dev(W.ravel()), to_dev(x.ravel())
+    ref, a = oracle.matvec(t, W, x, n, k, 8)
+    ones = [bits(run_mv(t, Wd, xd[j * k:], n, k, 1)) for j in range(8)]
+    for m in range(1, 9):
+        y = run_mv(t, Wd, xd, n, k, m)
+        check_tolerance(y.cpu().numpy().reshape(m, n), ref[0, :m], a[0, :m], f"k={k} m={m}")
+        yb = bits(y).reshape(m, n)
+        for j in range(m):
+            assert np.array_equal(yb[j], ones[j]), f"m={m} row {j} differs from its m=1 result"
+    base = bits(run_mv(t, Wd, xd, n, k, 3))
+    for nr in (1, 2, 4):
+        for waves, wgs in ((1, 1), (8, 2), (3, 5), (1, 1000), (4, 3)):
+            got = bits(run_mv(t, Wd, xd, n, k, 3, schedule=Schedule(1, nr, waves, wgs, 1 << 30)))
+            assert np.array_equal(got, base), f"nr={nr} waves={waves} wgs={wgs} changed the bits"

@@ -14,7 +14,8 @@ from gpu_util import bits, check_tolerance, oracle_sampled, run_mv, to_dev
 
 pytestmark = pytest.mark.gpu
 
-NAMES = [w.name for w in wl.WORKLOADS]
+NAMES = [w.name for w in wl.WORKLOADS if not w.experts]
+GATHER_NAMES = [w.name for w in wl.WORKLOADS if w.experts]
 
 
 def _sample_rows(n, count=24, seed=0):
@@ -71,3 +72,59 @@ def test_full_size_workload(name):
                     f"{name}: m={m} row {j} batch {b} differs from m=1"
         again = bits(run_mv(t, Wd, xd, n, k, m, batch, strides=strides))
         assert np.array_equal(again, ybits), f"{name}: m={m} not repeatable"
+
+
+@pytest.mark.parametrize("name", GATHER_NAMES)
+def test_full_size_gather_workload(name):
+    """Mixture-of-experts decode: every output against the oracle's gathered
+    product, bitwise against row_exact_mv on the selected expert, row-exact
+    across m and repeatable."""
+    w = wl.get(name)
+    t, n, k, batch, E = w.wtype, w.n, w.k, w.batch, w.experts
+    print(f"[workload] {name}: type {wl.TYPE_NAMES[t]} {E} experts of n={n} k={k}, {batch} selected, m={w.ms}",
+          flush=True)
+    W = w.make_weights()
+    ids = w.make_ids()
+    x = w.make_x(8)
+    Wd, xd = to_dev(W.ravel()), to_dev(x.ravel())
+    idd = torch.from_numpy(ids).to("cuda:0")
+    xrs, xbs, yrs, ybs = w.strides(8)
+    strides = qfr.Strides(xrs, xbs, yrs, ybs)
+    rb = qfr.row_exact_row_bytes(t, k)
+    ones = {}
+    for m in sorted(set(w.ms) | {1}):
+        _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, strides)
+        y = torch.full((yb // 4,), float("nan"), device="cuda:0")
+        qfr.row_exact_mv_gather(t, Wd, E, idd, xd, y, n, k, m, batch, strides)
+        torch.cuda.synchronize()
+        yc = y.cpu().numpy()
+        ref, a = oracle.matvec_gather(t, W, E, ids, x.ravel(), n, k, m, batch, xrs, xbs)
+        got = np.empty_like(ref)
+        for b in range(batch):
+            for j in range(m):
+                got[b, j] = yc[b * ybs + j * yrs: b * ybs + j * yrs + n]
+        ratio = check_tolerance(got, ref, a, f"{name} m={m}")
+        print(f"[workload] {name} m={m}: {batch} x {m} x {n} outputs ok, worst |err|/bound = {ratio:.3g}", flush=True)
+        ybits = bits(y)
+        if m == 1:
+            for j in range(8):
+                yj = torch.full((yb // 4,), float("nan"), device="cuda:0")
+                qfr.row_exact_mv_gather(t, Wd, E, idd, xd[j * xrs:], yj, n, k, 1, batch, strides)
+                torch.cuda.synchronize()
+                ones[j] = bits(yj)
+        for j in range(m):
+            for b in range(batch):
+                o = b * ybs + j * yrs
+                assert np.array_equal(ybits[o:o + n], ones[j][b * ybs:b * ybs + n]), \
+                    f"{name}: m={m} row {j} entry {b} differs from m=1"
+        # each entry equals the plain product with its expert's weights
+        for b in (0, batch - 1):
+            ye = run_mv(t, Wd.data_ptr() + int(ids[b]) * n * rb, xd, n, k, m, 1, strides=qfr.Strides(xrs, 0, n, 0))
+            yeb = bits(ye).reshape(m, n)
+            for j in range(m):
+                o = b * ybs + j * yrs
+                assert np.array_equal(ybits[o:o + n], yeb[j]), f"{name}: entry {b} row {j} differs from row_exact_mv"
+        again = torch.full((yb // 4,), float("nan"), device="cuda:0")
+        qfr.row_exact_mv_gather(t, Wd, E, idd, xd, again, n, k, m, batch, strides)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(again), ybits), f"{name}: m={m} not repeatable"

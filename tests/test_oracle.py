@@ -431,6 +431,31 @@ def test_matvec_vs_numpy_float64_dot():
     assert np.all(np.abs(y[0] - ref) <= 2 * k * 2.0 ** -53 * a[0])
 
 
+def test_gather_identity_and_selection():
+    """ids = 0..batch-1 is the plain batched product; a repeated id equals
+    the product with that weight set; an id out of range gives NaN only for
+    its own batch entry."""
+    t, E, n, k, m = wl.Q4_K, 5, 6, 256, 2
+    W = wl.weights(t, E * n, k, seed=81)
+    x = wl.activations(1, 4 * (m * k + 8), seed=82)[0]
+    xrs, xbs = k, m * k + 8
+    y, a = oracle.matvec(t, W, x, n, k, m, batch=4, x_row_stride=xrs, x_batch_stride=xbs)
+    yg, ag = oracle.matvec_gather(t, W, E, np.arange(4), x, n, k, m, 4, xrs, xbs)
+    assert np.array_equal(y, yg) and np.array_equal(a, ag)
+    rb = oracle.row_bytes(t, k)
+    ids = np.array([3, 3, -1, 4], np.int32)
+    yg, _ = oracle.matvec_gather(t, W, E, ids, x, n, k, m, 4, xrs, xbs)
+    for b, e in enumerate(ids):
+        if e < 0:
+            assert np.all(np.isnan(yg[b]))
+            continue
+        We = W.ravel()[e * n * rb:(e + 1) * n * rb]
+        ye, _ = oracle.matvec(t, We, x[b * xbs:], n, k, m, x_row_stride=xrs)
+        assert np.array_equal(yg[b], ye[0])
+    yg, _ = oracle.matvec_gather(t, W, E, np.array([0, 5, 1, 2], np.int32), x, n, k, m, 4, xrs, xbs)
+    assert np.all(np.isnan(yg[1])) and not np.any(np.isnan(yg[[0, 2, 3]]))
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributed():

@@ -160,6 +160,7 @@ class Workload:
     ms: Tuple[int, ...]
     index: int
     grouped: bool = False
+    experts: int = 0  # > 0: gathered product, batch entry b uses weight set ids[b] of `experts`
 
     @property
     def w_seed(self) -> int:
@@ -173,14 +174,28 @@ class Workload:
         """(x_row, x_batch, y_row, y_batch) in elements."""
         if self.grouped:
             return (self.batch * self.k, self.k, self.batch * self.n, self.n)
+        if self.experts:
+            # every selected expert multiplies the same tokens; y token-major [m, batch * n]
+            return (self.k, 0, self.batch * self.n, self.n)
         return (self.k, 0, self.n, 0)
 
     @property
     def weight_bytes(self) -> int:
+        """Weight bytes one call reads."""
         return row_bytes(self.wtype, self.k) * self.n * self.batch
 
+    @property
+    def stored_weight_bytes(self) -> int:
+        """Weight bytes held (every expert's set for a gathered product)."""
+        return row_bytes(self.wtype, self.k) * self.n * (self.experts or self.batch)
+
     def make_weights(self) -> np.ndarray:
-        return weights(self.wtype, self.n * self.batch, self.k, self.w_seed)
+        return weights(self.wtype, self.n * (self.experts or self.batch), self.k, self.w_seed)
+
+    def make_ids(self) -> np.ndarray:
+        """The batch entries' distinct expert ids (seeded), int32."""
+        u = Stream(3000 + self.index).uniform(self.experts)
+        return np.argsort(u, kind="stable")[:self.batch].astype(np.int32)
 
     def make_x(self, m: int = 8) -> np.ndarray:
         """x for ``m`` rows (drawn as 8 rows; an m-row run uses rows 0..m-1).
@@ -203,6 +218,8 @@ WORKLOADS: List[Workload] = [
     # dense weights under the same contract (a 4096 x 4096 projection)
     Workload("f32_4096x4096", F32, 4096, 4096, 1, (1, 4, 8), 6),
     Workload("bf16_4096x4096", BF16, 4096, 4096, 1, (1, 4, 8), 7),
+    # mixture-of-experts decode: 8 of 64 Q4_K experts (1408 x 2048) for the same tokens
+    Workload("q4_k_moe_64x1408x2048_top8", Q4_K, 1408, 2048, 8, (1, 4, 8), 8, experts=64),
 ]
 BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
 
