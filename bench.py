@@ -141,13 +141,23 @@ def main():
     xp = xd.data_ptr()
     yptrs = {m: ybufs[m].data_ptr() for m in ms}
     idd = torch.from_numpy(w.make_ids()).to(dev) if w.experts else None
-    if w.experts:  # checked path once
+    if w.fused_norm:
+        rd = torch.from_numpy(w.make_residual(8).ravel().copy()).to(dev)
+        gd = torch.from_numpy(w.make_norm_weight()).to(dev)
+        hd = torch.empty_like(rd)
+    if w.fused_norm:  # checked path once
+        qfr.row_exact_mv_add_rmsnorm(t, Wd[0], xd, rd, gd, 1e-5, hd, ybufs[ms[0]], n, k, ms[0], batch, strides,
+                                     stream=hs)
+    elif w.experts:
         qfr.row_exact_mv_gather(t, Wd[0], w.experts, idd, xd, ybufs[ms[0]], n, k, ms[0], batch, strides, stream=hs)
     else:
         qfr.row_exact_mv(t, Wd[0], xd, ybufs[ms[0]], n, k, ms[0], batch, strides, stream=hs)
 
     def launch(i, m):
-        if w.experts:
+        if w.fused_norm:
+            rc = lib.row_exact_mv_add_rmsnorm(int(t), wptrs[i % copies], xp, rd.data_ptr(), gd.data_ptr(),
+                                              ctypes.c_float(1e-5), hd.data_ptr(), yptrs[m], n, k, m, batch, sp, hs)
+        elif w.experts:
             rc = lib.row_exact_mv_gather(int(t), wptrs[i % copies], w.experts, idd.data_ptr(), xp, yptrs[m], n, k, m,
                                          batch, sp, hs)
         else:
@@ -353,10 +363,16 @@ def sweep(path, steps):
         Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
         xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
         idd = torch.from_numpy(w.make_ids()).cuda() if w.experts else None
+        if w.fused_norm:
+            rd = torch.from_numpy(w.make_residual(8).ravel().copy()).cuda()
+            gd = torch.from_numpy(w.make_norm_weight()).cuda()
+            hd = torch.empty_like(rd)
 
         def mv(i, y, m):
             if w.experts:
                 qfr.row_exact_mv_gather(t, Wd[i % copies], w.experts, idd, xd, y, n, k, m, batch, s)
+            elif w.fused_norm:
+                qfr.row_exact_mv_add_rmsnorm(t, Wd[i % copies], xd, rd, gd, 1e-5, hd, y, n, k, m, batch, s)
             else:
                 qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s)
 

@@ -173,6 +173,31 @@ int row_exact_mv_gather(row_exact_weight_t wt, const void *W, uint32_t num_exper
                         const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                         const row_exact_strides_t *strides, hipStream_t stream);
 
+/* The product with its input produced by a fused add + RMS normalisation:
+ *   h[b, j, :] = x[b, j, :] + r[b, j, :]                       (float32 adds)
+ *   x'[b, j, v] = h[b, j, v] / sqrt(mean_v h[b, j, v]^2 + eps) * g[v]
+ *   y[b, j, :] = W[b] . x'[b, j, :]
+ * (nuvec-core 0.6.0, src/gpu.rs, add_rms_norm / FastOp::AddRmsNorm: the sum
+ * x + r and its RMS normalisation with weight g, the step that produces the
+ * input of the next projection).  The mean is over the k values of each
+ * input row; its sum of squares is taken in float64 in a fixed order.  The
+ * normalisation is linear per row, so the product runs on u = h * g (float32)
+ * and each output is scaled once by the row's inverse RMS (float64, one
+ * rounding); y keeps the row-exact contract (bitwise the same for m = 1 and
+ * every row of m <= 8, for every packing).
+ *  x, r  : device float32, both in x's layout (strides as row_exact_mv).
+ *  g     : device float32[k], or NULL for no weight (g = 1).
+ *  eps   : finite, >= 0 (eps = 0 and an all-zero row give NaN outputs).
+ *  h     : device float32 in x's layout receiving x + r, or NULL.  Written
+ *          once (by one workgroup per batch entry); must not overlap x, r,
+ *          g, W or y.
+ *  r, g, h 16-byte aligned.  Other arguments as row_exact_mv.
+ * Errors: as row_exact_mv, plus ROW_EXACT_EARG (NULL r, bad eps),
+ * ROW_EXACT_EALIGN and ROW_EXACT_EALIAS for r, g and h. */
+int row_exact_mv_add_rmsnorm(row_exact_weight_t wt, const void *W, const float *x, const float *r, const float *g,
+                             float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                             const row_exact_strides_t *strides, hipStream_t stream);
+
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
  * depends on (wt, k) only; the packing fields may depend on every argument
  * and on the current device.  Writes *out; errors: EARG, EHIP. */

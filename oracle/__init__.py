@@ -67,6 +67,9 @@ def _load() -> ctypes.CDLL:
         lib.oracle_dequant.argtypes = [ctypes.c_int, P, u32, u32, P]
         lib.oracle_matvec_rows.restype = ctypes.c_int
         lib.oracle_matvec_rows.argtypes = [ctypes.c_int, P, P, u32, u32, u32, u32, u32, u32, u32, u32, P, P]
+        lib.oracle_mv_add_rmsnorm.restype = ctypes.c_int
+        lib.oracle_mv_add_rmsnorm.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, u32, u32, u32, u32, u32,
+                                              u32, P, P, P, P]
         lib.oracle_matvec_gather.restype = ctypes.c_int
         lib.oracle_matvec_gather.argtypes = [ctypes.c_int, P, u32, P, P, u32, u32, u32, u32, u32, u32, P, P]
         _lib = lib
@@ -172,3 +175,31 @@ def matvec_gather(wtype: int, W: np.ndarray, num_experts: int, ids: np.ndarray, 
     if rc != 0:
         raise ValueError(f"oracle_matvec_gather failed ({rc})")
     return y, a
+
+
+def mv_add_rmsnorm(wtype: int, W: np.ndarray, x: np.ndarray, r: np.ndarray, g: Optional[np.ndarray], eps: float,
+                   n: int, k: int, m: int, batch: int = 1, x_row_stride: Optional[int] = None,
+                   x_batch_stride: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Float64 reference of the product with a fused add + RMS norm of its
+    input: returns ``(h, xn, y, a)``; ``h`` (float32) in x's flat layout,
+    ``xn`` [batch, m, k] float64, ``y`` and ``a`` [batch, m, n]."""
+    lib = _load()
+    xrs = k if x_row_stride is None else x_row_stride
+    Wb = np.ascontiguousarray(W, dtype=np.uint8).ravel()
+    xf = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    rf = np.ascontiguousarray(r, dtype=np.float32).ravel()
+    need_x = (batch - 1) * x_batch_stride + (m - 1) * xrs + k
+    if Wb.size < row_bytes(wtype, k) * n * batch or xf.size < need_x or rf.size < need_x:
+        raise ValueError("oracle.mv_add_rmsnorm: buffers too small")
+    gf = None if g is None else np.ascontiguousarray(g, dtype=np.float32).ravel()
+    if gf is not None and gf.size < k:
+        raise ValueError("oracle.mv_add_rmsnorm: g too small")
+    h = np.full(xf.size, np.nan, dtype=np.float32)
+    xn = np.empty((batch, m, k), dtype=np.float64)
+    y = np.empty((batch, m, n), dtype=np.float64)
+    a = np.empty((batch, m, n), dtype=np.float64)
+    rc = lib.oracle_mv_add_rmsnorm(wtype, _ptr(Wb), _ptr(xf), _ptr(rf), None if gf is None else _ptr(gf), eps, n,
+                                   k, m, batch, xrs, x_batch_stride, _ptr(h), _ptr(xn), _ptr(y), _ptr(a))
+    if rc != 0:
+        raise ValueError(f"oracle_mv_add_rmsnorm failed ({rc})")
+    return h, xn, y, a

@@ -292,3 +292,53 @@ int oracle_matvec_gather(int type, const uint8_t *W, uint32_t num_experts, const
     }
     return 0;
 }
+
+/* The product with a fused add + RMS normalisation of its input (nuvec-core
+ * 0.6.0, src/gpu.rs, add_rms_norm: the sum x + r and its RMS normalisation
+ * with weight g).  For every batch b and input row j, over the k values v of
+ * the row (x, r and h share the layout b*xbs + j*xrs + v):
+ *   h[v]  = x[v] + r[v]                                  (float32 addition)
+ *   s     = sum_v h[v]^2                                 (float64, v in order)
+ *   xn[v] = h[v] / sqrt(s / k + eps) * g[v]              (float64; g NULL: 1)
+ *   y[(b*m + j)*n + i] = sum_v Wd[b*n + i][v] * xn[v]    (float64)
+ *   a[...]             = sum_v |Wd[b*n + i][v] * xn[v]|
+ * h is written in x's layout, xn dense [batch][m][k]. */
+int oracle_mv_add_rmsnorm(int type, const uint8_t *W, const float *x, const float *r, const float *g, float eps,
+                          uint32_t n, uint32_t k, uint32_t m, uint32_t batch, uint32_t xrs, uint32_t xbs,
+                          float *h, double *xn, double *y, double *a) {
+    if (!k_ok(type, k) || m == 0 || n == 0 || batch == 0) return -1;
+    uint64_t rb = oracle_row_bytes(type, k);
+    float *wd = (float *)malloc(sizeof(float) * k);
+    if (!wd) return -2;
+    for (uint32_t b = 0; b < batch; ++b) {
+        for (uint32_t j = 0; j < m; ++j) {
+            size_t off = (size_t)b * xbs + (size_t)j * xrs;
+            double *xr = xn + ((size_t)b * m + j) * k;
+            double s = 0.0;
+            for (uint32_t v = 0; v < k; ++v) {
+                float hv = x[off + v] + r[off + v];
+                h[off + v] = hv;
+                s += (double)hv * (double)hv;
+            }
+            double rms = sqrt(s / (double)k + (double)eps);
+            for (uint32_t v = 0; v < k; ++v) xr[v] = (double)h[off + v] / rms * (g ? (double)g[v] : 1.0);
+        }
+        for (uint32_t i = 0; i < n; ++i) {
+            const uint8_t *row = W + rb * ((uint64_t)b * n + i);
+            for (uint32_t v = 0; v < k; ++v) wd[v] = oracle_weight(type, row, v);
+            for (uint32_t j = 0; j < m; ++j) {
+                const double *xr = xn + ((size_t)b * m + j) * k;
+                double sy = 0.0, sa = 0.0;
+                for (uint32_t v = 0; v < k; ++v) {
+                    double p = (double)wd[v] * xr[v];
+                    sy += p;
+                    sa += fabs(p);
+                }
+                y[((size_t)b * m + j) * n + i] = sy;
+                a[((size_t)b * m + j) * n + i] = sa;
+            }
+        }
+    }
+    free(wd);
+    return 0;
+}

@@ -18,7 +18,8 @@ from typing import Any, Optional, Tuple
 __all__ = [
     "Weight", "Strides", "Schedule", "RowExactError", "LibraryMissing", "MAX_ROWS",
     "contiguous", "grouped_token_major", "library_path", "load_library",
-    "row_exact_mv", "row_exact_mv_scheduled", "row_exact_mv_gather", "row_exact_schedule", "row_exact_row_bytes",
+    "row_exact_mv", "row_exact_mv_scheduled", "row_exact_mv_gather", "row_exact_mv_add_rmsnorm",
+    "row_exact_schedule", "row_exact_row_bytes",
     "row_exact_required_bytes", "row_exact_dequant", "row_exact_last_error", "row_exact_launch_count",
     "row_exact_stream_read", "row_exact_stream_read_shapes",
 ]
@@ -114,6 +115,8 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_mv_scheduled.argtypes = [ctypes.c_int, P, P, P, u32, u32, u32, u32, SP, SchP, P]
     lib.row_exact_mv_gather.restype = ctypes.c_int
     lib.row_exact_mv_gather.argtypes = [ctypes.c_int, P, u32, P, P, P, u32, u32, u32, u32, SP, P]
+    lib.row_exact_mv_add_rmsnorm.restype = ctypes.c_int
+    lib.row_exact_mv_add_rmsnorm.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32, SP, P]
     lib.row_exact_schedule.restype = ctypes.c_int
     lib.row_exact_schedule.argtypes = [ctypes.c_int, u32, u32, u32, u32, SchP]
     lib.row_exact_row_bytes.restype = u64
@@ -231,6 +234,29 @@ def row_exact_mv_gather(wt: int, W: Any, num_experts: int, expert_ids: Any, x: A
     yp, _ = _ptr_and_bytes(y, "output")
     sp = ctypes.byref(strides) if strides is not None else None
     _check(lib.row_exact_mv_gather(int(wt), wp, num_experts, ip, xp, yp, n, k, m, batch, sp, _stream_handle(stream)))
+
+
+def row_exact_mv_add_rmsnorm(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int, k: int,
+                             m: int, batch: int = 1, strides: Optional[Strides] = None, stream: Any = None) -> None:
+    """Enqueue ``h = x + r``, ``x' = h / sqrt(mean(h^2) + eps) * g``,
+    ``y = W . x'`` per input row (see ``row_exact_mv_add_rmsnorm``); ``g`` and
+    ``h`` may be None."""
+    wt = Weight(wt)
+    lib = load_library()
+    _dtype_check(wt, W, x, y)
+    _size_check(wt, W, x, y, n, k, m, batch, strides)
+    _, xb, _ = row_exact_required_bytes(wt, n, k, m, batch, strides)
+    for t, need, name in ((r, xb, "r"), (h, xb, "h"), (g, 4 * k, "g")):
+        if t is None:
+            continue
+        _, have = _ptr_and_bytes(t, name)
+        if have is not None and have < need:
+            raise ValueError(f"{name} holds {have} bytes, needs {need}")
+    ptr = lambda t, name: None if t is None else _ptr_and_bytes(t, name)[0]
+    sp = ctypes.byref(strides) if strides is not None else None
+    _check(lib.row_exact_mv_add_rmsnorm(int(wt), ptr(W, "weight"), ptr(x, "input"), ptr(r, "r"), ptr(g, "g"),
+                                        float(eps), ptr(h, "h"), ptr(y, "output"), n, k, m, batch, sp,
+                                        _stream_handle(stream)))
 
 
 def row_exact_schedule(wt: int, n: int, k: int, m: int, batch: int = 1) -> Schedule:

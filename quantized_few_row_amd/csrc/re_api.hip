@@ -113,9 +113,14 @@ uint32_t xs_stride(int t, uint32_t kc) {
     return kc + 4 * ((kc + padp - 1) / padp);
 }
 
-size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
+// LDS of a workgroup: the m staged input rows (padded), then 4m doubles for
+// the fused normalisation's per-row partial sums.
+size_t lds_x_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
     const uint32_t kc = k_chunk < k ? k_chunk : k;
     return (size_t)m * xs_stride(t, kc) * sizeof(float);
+}
+size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
+    return lds_x_bytes(t, m, k, k_chunk) + (size_t)4 * m * sizeof(double);
 }
 
 typedef unsigned __int128 u128;
@@ -364,14 +369,46 @@ DqLauncher dq_launcher(int t) {
     }
 }
 
+// Inputs of the fused add + RMS normalisation.
+struct Norm {
+    const float *r, *g;
+    float *h;
+    float eps;
+};
+
+int validate_norm(const Norm &nm, const void *W, const float *x, const float *y, uint32_t k, uint32_t m,
+                  uint32_t batch, const row_exact_strides_t &s, uint64_t wb, uint64_t xbytes, uint64_t ybytes) {
+    if (!nm.r) return fail(ROW_EXACT_EARG, "r must be a non-NULL device pointer");
+    if (!(nm.eps >= 0.0f) || nm.eps > 3.4e38f) return fail(ROW_EXACT_EARG, "eps must be finite and >= 0");
+    if ((uintptr_t)nm.r % 16 || (uintptr_t)nm.g % 16 || (uintptr_t)nm.h % 16)
+        return fail(ROW_EXACT_EALIGN, "r, g and h must be 16-byte aligned");
+    (void)m;
+    (void)batch;
+    (void)s;
+    const uint64_t gb = nm.g ? 4ull * k : 0;
+    // r and h share x's layout and extent
+    if (overlap((uintptr_t)y, ybytes, (uintptr_t)nm.r, xbytes) || (nm.g && overlap((uintptr_t)y, ybytes, (uintptr_t)nm.g, gb)))
+        return fail(ROW_EXACT_EALIAS, "output range overlaps r or g");
+    if (nm.h && (overlap((uintptr_t)nm.h, xbytes, (uintptr_t)x, xbytes) ||
+                 overlap((uintptr_t)nm.h, xbytes, (uintptr_t)nm.r, xbytes) ||
+                 overlap((uintptr_t)nm.h, xbytes, (uintptr_t)W, wb) || overlap((uintptr_t)nm.h, xbytes, (uintptr_t)y, ybytes) ||
+                 (nm.g && overlap((uintptr_t)nm.h, xbytes, (uintptr_t)nm.g, gb))))
+        return fail(ROW_EXACT_EALIAS, "h overlaps x, r, g, W or y (other workgroups still read the inputs)");
+    return 0;
+}
+
 int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
         const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream,
-        const int32_t *ids = nullptr, uint32_t num_experts = 0) {
+        const int32_t *ids = nullptr, uint32_t num_experts = 0, const Norm *norm = nullptr) {
     g_err.clear();
     const row_exact_strides_t s = resolve_strides(strides, m, n, k);
     uint64_t wb, xbytes, ybytes;
     int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes, ids, num_experts);
     if (rc) return rc;
+    if (norm) {
+        rc = validate_norm(*norm, W, x, y, k, m, batch, s, wb, xbytes, ybytes);
+        if (rc) return rc;
+    }
     if (pin) {
         rc = check_schedule_fields(t, k, *pin);
         if (rc) return rc;
@@ -423,6 +460,11 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     a.xs_stride = xs_stride(t, a.kchunk);
     a.ids = ids;
     a.num_experts = num_experts;
+    a.r = norm ? norm->r : nullptr;
+    a.g = norm ? norm->g : nullptr;
+    a.h = norm ? norm->h : nullptr;
+    a.eps = norm ? norm->eps : 0.0f;
+    a.norm_offset = (uint32_t)lds_x_bytes(t, m, k, sch.k_chunk);
     const uint64_t grid_x = (uint64_t)wgs * batch;
     if (grid_x > 0x7fffffffull)
         return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);
@@ -460,6 +502,13 @@ int row_exact_mv_gather(row_exact_weight_t wt, const void *W, uint32_t num_exper
         return fail(ROW_EXACT_EARG, "expert_ids must be a non-NULL device pointer");
     }
     return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, expert_ids, num_experts);
+}
+
+int row_exact_mv_add_rmsnorm(row_exact_weight_t wt, const void *W, const float *x, const float *r, const float *g,
+                             float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                             const row_exact_strides_t *strides, hipStream_t stream) {
+    const Norm nm{r, g, h, eps};
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm);
 }
 
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,

@@ -29,6 +29,14 @@ struct MvArgs {
     uint32_t lpr_log2;          // log2 of the lanes per weight row (6, or 5 / 4 for short rows)
     const int32_t *ids;         // per-batch weight selection (NULL: batch b uses weights b)
     uint32_t num_experts;       // number of weight sets ids may select
+    // Fused add + RMS normalisation of the input (r != NULL): the product
+    // uses x' = (x + r) / sqrt(mean((x + r)^2) + eps) * g per input row; the
+    // sum x + r goes to h (if not NULL) from the first workgroup of a batch.
+    const float *r;
+    const float *g;             // k weights, or NULL for none
+    float *h;
+    float eps;
+    uint32_t norm_offset;       // byte offset in LDS of the m per-row inverse RMS values (double)
 };
 
 struct DqArgs {

@@ -411,6 +411,19 @@ template <> struct Tr<kQ6K> : Geo<kQ6K> {
     static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
 };
 
+// Per-row output scale of the fused normalisation (part == NULL: none).
+struct RowScale {
+    const double *part;
+    uint32_t k;
+    float eps;
+    __device__ __forceinline__ float apply(float v, uint32_t j) const {
+        if (!part) return v;
+        const double s = (part[4 * j] + part[4 * j + 1]) + (part[4 * j + 2] + part[4 * j + 3]);
+        const double inv = 1.0 / __builtin_sqrt(s / (double)k + (double)eps);
+        return (float)((double)v * inv);
+    }
+};
+
 // ---------------------------------------------------------------- reduction
 
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
@@ -436,7 +449,7 @@ constexpr int pow2ceil(int v) { return v <= 1 ? 1 : 2 * pow2ceil((v + 1) / 2); }
 // and store output (r, j) to y[j*yrs + row0 + r] when row0 + r < n.
 template <int M, int NR, int L>
 __device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *__restrict__ yb, uint32_t yrs,
-                                             uint32_t n, uint32_t row0, uint32_t lane) {
+                                             uint32_t n, uint32_t row0, uint32_t lane, const RowScale &sc) {
     // L lanes per weight row: slot lane / L of the wave holds rows
     // row0 + slot*NR + r.  The tree over a slot's lanes is the last log2(L)
     // levels of the 64-lane tree.
@@ -516,7 +529,7 @@ __device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *_
             if (o < (uint32_t)NA) {
                 const uint32_t r = o / M, j = o % M;
                 const uint32_t row = row0 + slot * NR + r;
-                if (row < n) yb[(uint64_t)j * yrs + row] = v[a];
+                if (row < n) yb[(uint64_t)j * yrs + row] = sc.apply(v[a], j);
             }
         }
     }
@@ -553,6 +566,105 @@ __device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__r
         }
     }
 }
+
+// ---------------------------------------------------------------- fused add + RMS norm
+//
+// nuvec-core 0.6.0, src/gpu.rs, add_rms_norm (FastOp::AddRmsNorm): the sum
+// h = x + r and its RMS normalisation h / sqrt(mean(h^2) + eps) * g, here
+// fused into the mat-vec.  The normalisation is linear in h per input row, so
+// the kernel stages u = h * g (one float32 rounding), runs the row-exact fma
+// chains and reduction on u, and scales each output once by the row's inverse
+// RMS: y = (float)((double)sum * inv).
+//
+// The statistic of input row j is summed in float64 in one fixed order: the
+// row's float4 chunks q are split over 256 virtual lanes (q mod 256), each
+// summing the squares of its chunks' h values in increasing q; each group of
+// 64 virtual lanes is reduced by a fixed xor tree, and the four group sums
+// are added as (s0 + s1) + (s2 + s3).  Workgroups with any number of waves
+// compute the same value (a wave takes whole 64-lane groups), and the single-
+// and multi-pass paths take the same steps, so outputs stay row-exact.
+//
+// LDS layout after the staged x: part[M][4] (double).
+
+__device__ __forceinline__ double shfl_xor_d(double v, int mask) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)u, mask, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(u >> 32), mask, 64);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double fold4(double ss, f32x4 h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss = __builtin_fma((double)h[i], (double)h[i], ss);
+    return ss;
+}
+
+__device__ __forceinline__ f32x4 times_g(f32x4 h, const float *__restrict__ g, uint32_t v) {
+    if (!g) return h;
+    const f32x4 gv = *(const f32x4 *)(g + v);
+    f32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = h[i] * gv[i];
+    return u;
+}
+
+// The four group sums of every input row into part[j*4 + group], with
+// h = x + r read from memory; h is also written to hb (when not NULL; every
+// chunk is visited exactly once) and, with TO_LDS, u = h * g staged into xs
+// in the padded x layout (single pass).  A wave takes tasks (row, group)
+// wave, wave + nwaves, ... one after the other (interleaving several tasks
+// measured slower: the extra registers cost every instance occupancy).
+template <int T, int M, bool TO_LDS>
+__device__ __forceinline__ void norm_partials(double *part, float *__restrict__ xs, uint32_t XS,
+                                              const float *__restrict__ xb, const float *__restrict__ rb,
+                                              const float *__restrict__ g, float *__restrict__ hb, uint32_t xrs,
+                                              uint32_t k, uint32_t wave, uint32_t nwaves, uint32_t lane) {
+    const uint32_t n4 = k >> 2;
+    for (uint32_t task = wave; task < 4u * M; task += nwaves) {
+        const uint32_t j = task >> 2, grp = task & 3;
+        double ss = 0.0;
+#pragma unroll 4
+        for (uint32_t q = grp * 64 + lane; q < n4; q += 256) {
+            const f32x4 xv = *(const f32x4 *)(xb + (uint64_t)j * xrs + 4 * q);
+            const f32x4 rv = *(const f32x4 *)(rb + (uint64_t)j * xrs + 4 * q);
+            f32x4 h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = xv[i] + rv[i];
+            if (hb) *(f32x4 *)(hb + (uint64_t)j * xrs + 4 * q) = h;
+            if constexpr (TO_LDS) {
+                const uint32_t lv = 4 * q;
+                *(f32x4 *)(xs + j * XS + lv + 4 * (lv / Geo<T>::PADP)) = times_g(h, g, lv);
+            }
+            ss = fold4(ss, h);
+        }
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) ss += shfl_xor_d(ss, msk);
+        if (lane == 0) part[task] = ss;
+    }
+}
+
+// Multi-pass: stage values [v0, v1) of u = (x + r) * g.
+template <int T, int M>
+__device__ __forceinline__ void stage_u(float *__restrict__ xs, const float *__restrict__ xb,
+                                        const float *__restrict__ rb, const float *__restrict__ g, uint32_t xrs,
+                                        uint32_t v0, uint32_t v1, uint32_t XS) {
+    const uint32_t n4 = (v1 - v0) >> 2;
+    for (uint32_t q = threadIdx.x; q < n4; q += blockDim.x) {
+        const uint32_t v = v0 + 4 * q;
+        const uint32_t lv = 4 * q;
+        const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const f32x4 xv = *(const f32x4 *)(xb + (uint64_t)j * xrs + v);
+            const f32x4 rv = *(const f32x4 *)(rb + (uint64_t)j * xrs + v);
+            f32x4 h;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = xv[i] + rv[i];
+            *(f32x4 *)(xs + j * XS + d) = times_g(h, g, v);
+        }
+    }
+}
+
 
 // ---------------------------------------------------------------- one piece
 
@@ -691,14 +803,14 @@ __device__ __forceinline__ void load_item(const uint8_t *Wb, const MvArgs &a, ui
 // The group's outputs, with the tree for the lanes-per-row of this k.
 template <int M, int NR, bool SUB>
 __device__ __forceinline__ void store_group(const MvArgs &a, const float (&acc)[NR][M], float *__restrict__ yb,
-                                            uint32_t g, uint32_t lane) {
+                                            uint32_t g, uint32_t lane, const RowScale &sc) {
     const uint32_t row0 = (g * NR) << (6 - lpr_of<SUB>(a));
     if constexpr (!SUB)
-        reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, row0, lane);
+        reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, row0, lane, sc);
     else if (a.lpr_log2 == 5)
-        reduce_store<M, NR, 32>(acc, yb, a.yrs, a.n, row0, lane);
+        reduce_store<M, NR, 32>(acc, yb, a.yrs, a.n, row0, lane, sc);
     else
-        reduce_store<M, NR, 16>(acc, yb, a.yrs, a.n, row0, lane);
+        reduce_store<M, NR, 16>(acc, yb, a.yrs, a.n, row0, lane, sc);
 }
 
 template <int M, int NR> __device__ __forceinline__ void zero(float (&acc)[NR][M]) {
@@ -725,7 +837,7 @@ template <int T, int M, int NR, bool SUB>
 __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__restrict__ Wb, float *__restrict__ yb,
                                           const float *__restrict__ xs, uint32_t XS, uint32_t &lg, uint32_t &ls,
                                           uint32_t &cg, uint32_t &cs, uint32_t gstride, uint32_t g1, uint32_t S,
-                                          uint32_t lane, uint32_t li, uint32_t slot,
+                                          uint32_t lane, uint32_t li, uint32_t slot, const RowScale &sc,
                                           const typename Tr<T>::Raw (&cur)[NR], typename Tr<T>::Raw (&nxt)[NR],
                                           float (&acc)[NR][M]) {
     if (lg < g1) {
@@ -738,7 +850,7 @@ __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__rest
     const uint32_t pc = (cs << lpr_of<SUB>(a)) + li;
     if (pc < a.pieces) compute_piece<T, M, NR>(acc, cur, pc, 0, xs, XS, a.k);
     if (cs == S - 1) {
-        store_group<M, NR, SUB>(a, acc, yb, cg, lane);
+        store_group<M, NR, SUB>(a, acc, yb, cg, lane, sc);
         zero<M, NR>(acc);
     }
     if (++cs == S) {
@@ -751,8 +863,10 @@ __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__rest
 // ---------------------------------------------------------------- kernels
 
 // SUB: instances for short rows (32 or 16 lanes per row, a.lpr_log2 5 / 4);
-// the others have 64 lanes per row as compile-time constants.
-template <int T, int M, int NR, bool SUB>
+// the others have 64 lanes per row as compile-time constants.  NORM: the
+// instances with the fused add + RMS normalisation (a.r != NULL); kept apart
+// so that its prologue's registers do not cost the plain product occupancy.
+template <int T, int M, int NR, bool SUB, bool NORM>
 __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     extern __shared__ float xs[];
     const uint32_t lane = threadIdx.x & 63u;
@@ -809,20 +923,26 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 lg += nwaves;
             }
         }
-        stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
+        double *part = (double *)((uint8_t *)xs + a.norm_offset);
+        const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
+        if constexpr (NORM)
+            norm_partials<T, M, true>(part, xs, XS, xb, a.r + b * a.xbs, a.g,
+                                      (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);
+        else
+            stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
         __syncthreads();
         if (gfirst < g1) {
             float acc[NR][M];
             zero<M, NR>(acc);
             uint32_t cg = gfirst, cs = 0;
             if constexpr (DEPTH == 2) {
-                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, A, C, acc) &&
-                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, B, A, acc) &&
-                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, C, B, acc)) {
+                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, A, C, acc) &&
+                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, B, A, acc) &&
+                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, C, B, acc)) {
                 }
             } else {
-                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, A, B, acc) &&
-                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, B, A, acc)) {
+                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, A, B, acc) &&
+                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, B, A, acc)) {
                 }
             }
         }
@@ -830,6 +950,12 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         // Several LDS passes over K (only for rows of more than 64 pieces, so
         // 64 lanes per row): every wave of the workgroup works on one row
         // group per round and all waves stage each pass together.
+        double *part = (double *)((uint8_t *)xs + a.norm_offset);
+        const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
+        const float *rb = NORM ? a.r + b * a.xbs : nullptr;
+        if constexpr (NORM)  // the pass loop's first barrier orders these writes before any store
+            norm_partials<T, M, false>(part, nullptr, XS, xb, rb, a.g, (a.h && w == 0) ? a.h + b * a.xbs : nullptr,
+                                       a.xrs, a.k, wave, nwaves, lane);
         for (uint32_t base = g0; base < g1; base += nwaves) {
             const uint32_t g = base + wave;
             const bool active = g < g1;
@@ -844,11 +970,14 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 const uint32_t vb = pb * Geo<T>::PV;
                 const uint32_t ve = min(a.k, vb + a.kchunk);
                 __syncthreads();
-                stage_x<T, M>(xs, xb, a.xrs, vb, ve, XS);
+                if constexpr (NORM)
+                    stage_u<T, M>(xs, xb, rb, a.g, a.xrs, vb, ve, XS);
+                else
+                    stage_x<T, M>(xs, xb, a.xrs, vb, ve, XS);
                 __syncthreads();
                 if (active) accumulate<T, M, NR>(acc, R, o0, pb, pe, vb, xs, XS, a.k, lane);
             }
-            if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane);
+            if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane, sc);
         }
     }
 }
@@ -880,7 +1009,10 @@ __global__ void __launch_bounds__(256) dq_kernel(const DqArgs a) {
 
 template <int T, int M, int NR>
 hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    const void *fn = a.lpr_log2 < 6 ? (const void *)mv_kernel<T, M, NR, true> : (const void *)mv_kernel<T, M, NR, false>;
+    const void *fn = a.lpr_log2 < 6 ? (a.r ? (const void *)mv_kernel<T, M, NR, true, true>
+                                           : (const void *)mv_kernel<T, M, NR, true, false>)
+                                    : (a.r ? (const void *)mv_kernel<T, M, NR, false, true>
+                                           : (const void *)mv_kernel<T, M, NR, false, false>);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -892,7 +1024,7 @@ hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStr
 
 template <int T, int M, int NR>
 hipError_t attributes_one(hipFuncAttributes *attr) {
-    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR, false>);
+    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR, false, false>);
 }
 
 template <int T, int M>

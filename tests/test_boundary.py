@@ -36,7 +36,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = qfr.load_library()
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 12, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -255,3 +255,34 @@ def test_gather_weight_extent_counts_expert_sets():
     y = WP + 4 * 64 * rb
     rc, msg = _gather(num_experts=5, y=y, ids=XP + 0x100000)
     assert rc == -4 and "overlaps" in msg
+
+
+RP, GP, HP = 0x7F3000000000, 0x7F4000000000, 0x7F5000000000
+
+
+def _norm(r=RP, g=GP, h=HP, eps=1e-5, x=XP, y=YP, W=WP, n=64, k=256, m=4, wt=Weight.Q8_0):
+    lib = qfr.load_library()
+    rc = lib.row_exact_mv_add_rmsnorm(int(wt), W, x, r, g, eps, h, y, n, k, m, 1, None, None)
+    return rc, qfr.row_exact_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(r=0), -1, "r must be"),
+    (dict(eps=-1.0), -1, "eps"),
+    (dict(eps=float("nan")), -1, "eps"),
+    (dict(eps=float("inf")), -1, "eps"),
+    (dict(r=RP + 4), -2, "16-byte"),
+    (dict(g=GP + 8), -2, "16-byte"),
+    (dict(h=HP + 4), -2, "16-byte"),
+    (dict(h=XP + 16), -4, "h overlaps"),
+    (dict(h=RP), -4, "h overlaps"),
+    (dict(h=YP), -4, "overlap"),
+    (dict(r=YP), -4, "overlaps"),
+    (dict(m=9), -1, "m (9)"),
+])
+def test_add_rmsnorm_invalid_arguments(kw, code, text):
+    before = qfr.row_exact_launch_count()
+    rc, msg = _norm(**kw)
+    assert rc == code, (rc, msg)
+    assert text in msg, msg
+    assert qfr.row_exact_launch_count() == before

@@ -1,0 +1,113 @@
+"""GPU parity of the product with a fused add + RMS normalisation of its
+input (row_exact_mv_add_rmsnorm) against the oracle: h = x + r bit-exact,
+y within the tolerance of the float64 reference, row exactness across m and
+packing inertness (single and multi-pass LDS staging), with and without g,
+batched strides."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_few_row_amd as qfr
+import workloads as wl
+from gpu_util import bits, check_tolerance, to_dev
+from quantized_few_row_amd import Strides
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {wl.F16: (41, 1028), wl.Q8_0: (45, 4160), wl.Q4_K: (37, 4352), wl.Q6_K: (29, 4352), wl.Q5_0: (33, 2112),
+          wl.F32: (35, 516), wl.BF16: (39, 1028)}
+TYPES = list(SHAPES)
+IDS = [wl.TYPE_NAMES[t] for t in TYPES]
+
+
+def _run(t, Wd, xd, rd, gd, eps, n, k, m, batch=1, strides=None):
+    _, xb, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, strides)
+    y = torch.full((yb // 4,), float("nan"), device="cuda:0")
+    h = torch.full((xb // 4,), float("nan"), device="cuda:0")
+    qfr.row_exact_mv_add_rmsnorm(t, Wd, xd, rd, gd, eps, h, y, n, k, m, batch, strides)
+    torch.cuda.synchronize()
+    return h, y
+
+
+@pytest.mark.parametrize("t", TYPES, ids=IDS)
+@pytest.mark.parametrize("with_g", [True, False])
+def test_add_rmsnorm_parity(t, with_g):
+    n, k = SHAPES[t]
+    W = wl.weights(t, n, k, seed=970 + t)
+    x = wl.activations(8, k, seed=971 + t)
+    r = wl.activations(8, k, seed=972 + t)
+    g = (1.0 + 0.1 * wl.activations(1, k, seed=973 + t)[0]).astype(np.float32) if with_g else None
+    eps = 1e-5
+    Wd, xd, rd = to_dev(W.ravel()), to_dev(x.ravel()), to_dev(r.ravel())
+    gd = to_dev(g) if with_g else None
+    href, _, yref, a = oracle.mv_add_rmsnorm(t, W, x, r, g, eps, n, k, 8)
+    ones = []
+    for j in range(8):
+        _, y1 = _run(t, Wd, xd[j * k:], rd[j * k:], gd, eps, n, k, 1)
+        ones.append(bits(y1))
+    for m in (1, 2, 3, 5, 8):
+        h, y = _run(t, Wd, xd, rd, gd, eps, n, k, m)
+        assert np.array_equal(bits(h), href[:m * k].view(np.int32)), f"m={m}: h differs from x + r"
+        check_tolerance(y.cpu().numpy().reshape(1, m, n), yref[:, :m], a[:, :m], f"m={m}")
+        yb = bits(y).reshape(m, n)
+        for j in range(m):
+            assert np.array_equal(yb[j], ones[j]), f"m={m} row {j} differs from its m=1 result"
+    again = bits(_run(t, Wd, xd, rd, gd, eps, n, k, 8)[1])
+    assert np.array_equal(again, bits(_run(t, Wd, xd, rd, gd, eps, n, k, 8)[1]))
+
+
+@pytest.mark.parametrize("t", [wl.Q8_0, wl.Q4_K, wl.F16], ids=["Q8_0", "Q4_K", "F16"])
+def test_add_rmsnorm_batched_strided(t):
+    """Batch-major strided x / r / h with gaps: per-row statistics, h written
+    once per element, nothing outside the views touched."""
+    n, k = SHAPES[t]
+    batch, m = 3, 4
+    s = Strides(k + 8, 5 * (k + 8), n + 3, 5 * (n + 3))
+    W = wl.weights(t, n * batch, k, seed=980 + t)
+    _, xb, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, s)
+    x = wl.activations(1, xb // 4, seed=981 + t)[0]
+    r = wl.activations(1, xb // 4, seed=982 + t)[0]
+    g = (1.0 + 0.1 * wl.activations(1, k, seed=983 + t)[0]).astype(np.float32)
+    h = torch.full((xb // 4 + 8,), 7.0, device="cuda:0")
+    y = torch.full((yb // 4 + 8,), 7.0, device="cuda:0")
+    qfr.row_exact_mv_add_rmsnorm(t, to_dev(W.ravel()), to_dev(x), to_dev(r), to_dev(g), 1e-6, h, y, n, k, m, batch, s)
+    torch.cuda.synchronize()
+    href, _, yref, a = oracle.mv_add_rmsnorm(t, W, x, r, g, 1e-6, n, k, m, batch, s.x_row_stride, s.x_batch_stride)
+    hc, yc = h.cpu().numpy(), y.cpu().numpy()
+    hmask = np.zeros(hc.size, bool)
+    for b in range(batch):
+        for j in range(m):
+            o = b * s.x_batch_stride + j * s.x_row_stride
+            hmask[o:o + k] = True
+    assert np.array_equal(hc[hmask].view(np.uint32), href[hmask[:href.size]].view(np.uint32))
+    assert np.all(hc[~hmask] == 7.0), "h written outside its view"
+    got = np.empty((batch, m, n))
+    ymask = np.zeros(yc.size, bool)
+    for b in range(batch):
+        for j in range(m):
+            o = b * s.y_batch_stride + j * s.y_row_stride
+            got[b, j] = yc[o:o + n]
+            ymask[o:o + n] = True
+    check_tolerance(got, yref, a, "batched")
+    assert np.all(yc[~ymask] == 7.0), "y written outside its view"
+
+
+def test_add_rmsnorm_multipass_matches_single_pass():
+    """k = 14336 at m = 8 does not fit LDS in one pass (the fused statistic is
+    taken before the passes); every row equals its m = 1 (single-pass) run."""
+    t, n, k = wl.Q6_K, 9, 14336
+    W = wl.weights(t, n, k, seed=990)
+    x = wl.activations(8, k, seed=991)
+    r = wl.activations(8, k, seed=992)
+    g = (1.0 + 0.1 * wl.activations(1, k, seed=993)[0]).astype(np.float32)
+    Wd, xd, rd, gd = to_dev(W.ravel()), to_dev(x.ravel()), to_dev(r.ravel()), to_dev(g)
+    assert qfr.row_exact_schedule(t, n, k, 8).k_chunk < k and qfr.row_exact_schedule(t, n, k, 1).k_chunk >= k
+    _, yref, a = oracle.mv_add_rmsnorm(t, W, x, r, g, 1e-5, n, k, 8)[1:]
+    h8, y8 = _run(t, Wd, xd, rd, gd, 1e-5, n, k, 8)
+    check_tolerance(y8.cpu().numpy().reshape(1, 8, n), yref, a, "m=8 multi-pass")
+    y8b = bits(y8).reshape(8, n)
+    for j in range(8):
+        _, y1 = _run(t, Wd, xd[j * k:], rd[j * k:], gd, 1e-5, n, k, 1)
+        assert np.array_equal(bits(y1), y8b[j]), f"row {j}: multi-pass m=8 differs from single-pass m=1"
+    assert np.array_equal(h8.cpu().numpy(), (x + r).ravel())

@@ -14,7 +14,8 @@ from gpu_util import bits, check_tolerance, oracle_sampled, run_mv, to_dev
 
 pytestmark = pytest.mark.gpu
 
-NAMES = [w.name for w in wl.WORKLOADS if not w.experts]
+NAMES = [w.name for w in wl.WORKLOADS if not w.experts and not w.fused_norm]
+NORM_NAMES = [w.name for w in wl.WORKLOADS if w.fused_norm]
 GATHER_NAMES = [w.name for w in wl.WORKLOADS if w.experts]
 
 
@@ -128,3 +129,32 @@ def test_full_size_gather_workload(name):
         qfr.row_exact_mv_gather(t, Wd, E, idd, xd, again, n, k, m, batch, strides)
         torch.cuda.synchronize()
         assert np.array_equal(bits(again), ybits), f"{name}: m={m} not repeatable"
+
+
+@pytest.mark.parametrize("name", NORM_NAMES)
+def test_full_size_fused_norm_workload(name):
+    """The projection with its input made by the fused add + RMS norm: h
+    bit-exact, every output against the oracle, row-exact across m."""
+    w = wl.get(name)
+    t, n, k = w.wtype, w.n, w.k
+    print(f"[workload] {name}: type {wl.TYPE_NAMES[t]} n={n} k={k} m={w.ms}, fused add + RMS norm", flush=True)
+    W, x, r, g = w.make_weights(), w.make_x(8), w.make_residual(8), w.make_norm_weight()
+    Wd, xd, rd, gd = to_dev(W.ravel()), to_dev(x.ravel()), to_dev(r.ravel()), to_dev(g)
+    href, _, yref, a = oracle.mv_add_rmsnorm(t, W, x, r, g, 1e-5, n, k, 8)
+    ones = []
+    for j in range(8):
+        y1 = torch.empty(n, device="cuda:0")
+        qfr.row_exact_mv_add_rmsnorm(t, Wd, xd[j * k:], rd[j * k:], gd, 1e-5, None, y1, n, k, 1)
+        torch.cuda.synchronize()
+        ones.append(bits(y1))
+    for m in w.ms:
+        y = torch.full((m * n,), float("nan"), device="cuda:0")
+        h = torch.full((m * k,), float("nan"), device="cuda:0")
+        qfr.row_exact_mv_add_rmsnorm(t, Wd, xd, rd, gd, 1e-5, h, y, n, k, m)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(h), href[:m * k].view(np.int32)), f"m={m}: h"
+        ratio = check_tolerance(y.cpu().numpy().reshape(1, m, n), yref[:, :m], a[:, :m], f"{name} m={m}")
+        print(f"[workload] {name} m={m}: {m} x {n} outputs ok, worst |err|/bound = {ratio:.3g}", flush=True)
+        yb = bits(y).reshape(m, n)
+        for j in range(m):
+            assert np.array_equal(yb[j], ones[j]), f"{name}: m={m} row {j} differs from m=1"

@@ -456,6 +456,32 @@ def test_gather_identity_and_selection():
     assert np.all(np.isnan(yg[1])) and not np.any(np.isnan(yg[[0, 2, 3]]))
 
 
+def test_add_rmsnorm_sum_and_normalisation():
+    """h is numpy's float32 sum; with eps = 0 and g = 1 every normalised row
+    has mean square 1; a constant row c normalises to c / sqrt(c^2 + eps);
+    scaling h by 4 leaves xn unchanged (eps = 0, exact in float64); the
+    product is a library float64 dot of the dequantized weights with xn."""
+    t, n, k, m = wl.Q8_0, 5, 64, 3
+    W = wl.weights(t, n, k, seed=91)
+    x = wl.activations(m, k, seed=92)
+    r = wl.activations(m, k, seed=93)
+    g = (1.0 + wl.activations(1, k, seed=94)[0] * 0.1).astype(np.float32)
+    h, xn, y, a = oracle.mv_add_rmsnorm(t, W, x, r, None, 0.0, n, k, m)
+    assert np.array_equal(_bits32(h), _bits32((x + r).ravel()))
+    assert np.allclose((xn[0] ** 2).mean(axis=1), 1.0, rtol=1e-14, atol=0)
+    _, xn4, _, _ = oracle.mv_add_rmsnorm(t, W, 4 * x, 4 * r, None, 0.0, n, k, m)
+    assert np.array_equal(xn4, xn)
+    c, eps = np.float32(0.75), 1e-3
+    _, xc, _, _ = oracle.mv_add_rmsnorm(t, W, np.full((1, k), c, np.float32), np.zeros((1, k), np.float32), g, eps,
+                                        n, k, 1)
+    assert np.allclose(xc[0, 0], float(c) / np.sqrt(float(c) ** 2 + eps) * g.astype(np.float64), rtol=1e-15)
+    h, xn, y, a = oracle.mv_add_rmsnorm(t, W, x, r, g, 1e-5, n, k, m)
+    wd = oracle.dequant(t, W, n, k).astype(np.float64)
+    ref = xn[0] @ wd.T
+    assert np.all(np.abs(y[0] - ref) <= 2 * k * 2.0 ** -53 * a[0])
+    assert np.all(np.abs(a[0] - np.abs(xn[0]) @ np.abs(wd).T) <= 2 * k * 2.0 ** -53 * a[0])
+
+
 # ---------------------------------------------------------------- generator
 
 def test_generator_deterministic_and_distributed():

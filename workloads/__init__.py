@@ -161,6 +161,7 @@ class Workload:
     index: int
     grouped: bool = False
     experts: int = 0  # > 0: gathered product, batch entry b uses weight set ids[b] of `experts`
+    fused_norm: bool = False  # input produced by the fused add + RMS norm (x + r, weight g)
 
     @property
     def w_seed(self) -> int:
@@ -192,6 +193,15 @@ class Workload:
     def make_weights(self) -> np.ndarray:
         return weights(self.wtype, self.n * (self.experts or self.batch), self.k, self.w_seed)
 
+    def make_residual(self, m: int = 8) -> np.ndarray:
+        """r for the fused add + RMS norm, shaped like make_x (seed 4000 + index)."""
+        cols = self.batch * self.k if self.grouped else self.k
+        return activations(8, cols, 4000 + self.index)[:m].copy()
+
+    def make_norm_weight(self) -> np.ndarray:
+        """g for the fused add + RMS norm: 1 + 0.1 N(0, 1), float32 (seed 5000 + index)."""
+        return (1.0 + 0.1 * Stream(5000 + self.index).normal(self.k)).astype(np.float32)
+
     def make_ids(self) -> np.ndarray:
         """The batch entries' distinct expert ids (seeded), int32."""
         u = Stream(3000 + self.index).uniform(self.experts)
@@ -220,6 +230,8 @@ WORKLOADS: List[Workload] = [
     Workload("bf16_4096x4096", BF16, 4096, 4096, 1, (1, 4, 8), 7),
     # mixture-of-experts decode: 8 of 64 Q4_K experts (1408 x 2048) for the same tokens
     Workload("q4_k_moe_64x1408x2048_top8", Q4_K, 1408, 2048, 8, (1, 4, 8), 8, experts=64),
+    # the Q8_0 projection with its input made by the fused add + RMS norm (eps 1e-5)
+    Workload("q8_0_4096x4096_add_rmsnorm", Q8_0, 4096, 4096, 1, (1, 4, 8), 9, fused_norm=True),
 ]
 BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
 
