@@ -50,6 +50,7 @@
 #define REX_DEPTH_BUDGET 120
 #endif
 
+
 namespace rex {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -821,7 +822,8 @@ template <int M, int NR> __device__ __forceinline__ void zero(float (&acc)[NR][M
 }
 
 // Items in flight ahead of the one being multiplied (1 or 2), chosen so the
-// raw buffers of 1 + DEPTH items stay within the register budget.
+// raw buffers of 1 + DEPTH items stay within the register budget (a third
+// item in flight measured no faster at m <= 2).
 template <int T, int M, int NR> struct Depth {
     static constexpr int raw_dwords = (int)(sizeof(typename Tr<T>::Raw) / 4) * NR;
     static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= REX_DEPTH_BUDGET) ? 2 : 1;
@@ -909,20 +911,17 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         uint32_t lg = g0 + wave, ls = 0;
         const uint32_t gfirst = lg;
         Raw A[NR], B[NR], C[NR];
-        if (lg < g1) {
-            load_item<T, NR, SUB>(Wb, a, lg, min(li, a.pieces - 1), slot, A);
-            if (++ls == S) {
-                ls = 0;
-                lg += nwaves;
+        auto prefetch = [&](Raw(&dst)[NR]) {
+            if (lg < g1) {
+                load_item<T, NR, SUB>(Wb, a, lg, min((ls << lpr) + li, a.pieces - 1), slot, dst);
+                if (++ls == S) {
+                    ls = 0;
+                    lg += nwaves;
+                }
             }
-        }
-        if (DEPTH == 2 && lg < g1) {
-            load_item<T, NR, SUB>(Wb, a, lg, min((ls << lpr) + li, a.pieces - 1), slot, B);
-            if (++ls == S) {
-                ls = 0;
-                lg += nwaves;
-            }
-        }
+        };
+        prefetch(A);
+        if (DEPTH == 2) prefetch(B);
         double *part = (double *)((uint8_t *)xs + a.norm_offset);
         const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
         if constexpr (NORM)
