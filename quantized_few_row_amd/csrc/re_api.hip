@@ -376,17 +376,15 @@ struct Norm {
     float eps;
 };
 
-int validate_norm(const Norm &nm, const void *W, const float *x, const float *y, uint32_t k, uint32_t m,
-                  uint32_t batch, const row_exact_strides_t &s, uint64_t wb, uint64_t xbytes, uint64_t ybytes) {
+// r, g, h against each other and the product's operands; r and h have x's
+// layout, so x's byte extent.
+int validate_norm(const Norm &nm, const void *W, const float *x, const float *y, uint32_t k, uint64_t wb,
+                  uint64_t xbytes, uint64_t ybytes) {
     if (!nm.r) return fail(ROW_EXACT_EARG, "r must be a non-NULL device pointer");
     if (!(nm.eps >= 0.0f) || nm.eps > 3.4e38f) return fail(ROW_EXACT_EARG, "eps must be finite and >= 0");
     if ((uintptr_t)nm.r % 16 || (uintptr_t)nm.g % 16 || (uintptr_t)nm.h % 16)
         return fail(ROW_EXACT_EALIGN, "r, g and h must be 16-byte aligned");
-    (void)m;
-    (void)batch;
-    (void)s;
     const uint64_t gb = nm.g ? 4ull * k : 0;
-    // r and h share x's layout and extent
     if (overlap((uintptr_t)y, ybytes, (uintptr_t)nm.r, xbytes) || (nm.g && overlap((uintptr_t)y, ybytes, (uintptr_t)nm.g, gb)))
         return fail(ROW_EXACT_EALIAS, "output range overlaps r or g");
     if (nm.h && (overlap((uintptr_t)nm.h, xbytes, (uintptr_t)x, xbytes) ||
@@ -406,7 +404,7 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes, ids, num_experts);
     if (rc) return rc;
     if (norm) {
-        rc = validate_norm(*norm, W, x, y, k, m, batch, s, wb, xbytes, ybytes);
+        rc = validate_norm(*norm, W, x, y, k, wb, xbytes, ybytes);
         if (rc) return rc;
     }
     if (pin) {

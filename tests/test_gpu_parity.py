@@ -205,3 +205,15 @@ def test_short_rows_lane_maps(t, k):
         for waves, wgs in ((1, 1), (8, 2), (3, 5), (1, 1000), (4, 3)):
             got = bits(run_mv(t, Wd, xd, n, k, 3, schedule=Schedule(1, nr, waves, wgs, 1 << 30)))
             assert np.array_equal(got, base), f"nr={nr} waves={waves} wgs={wgs} changed the bits"
+
+
+def test_stream_read_probe_runs_every_shape():
+    """The read probe (a measurement aid) accepts every shape on a device
+    buffer, including a size that is not a whole KiB."""
+    buf = torch.ones(3 * 1024 * 1024 + 48, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    before = qfr.row_exact_launch_count()
+    for shape in range(qfr.row_exact_stream_read_shapes()):
+        qfr.row_exact_stream_read(buf, buf.numel() // 16 * 16, sink, shape)
+    torch.cuda.synchronize()
+    assert qfr.row_exact_launch_count() == before + qfr.row_exact_stream_read_shapes()
