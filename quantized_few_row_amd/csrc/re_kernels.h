@@ -612,35 +612,96 @@ __device__ __forceinline__ f32x4 times_g(f32x4 h, const float *__restrict__ g, u
 // The four group sums of every input row into part[j*4 + group], with
 // h = x + r read from memory; h is also written to hb (when not NULL; every
 // chunk is visited exactly once) and, with TO_LDS, u = h * g staged into xs
-// in the padded x layout (single pass).  A wave takes tasks (row, group)
-// wave, wave + nwaves, ... one after the other (interleaving several tasks
-// measured slower: the extra registers cost every instance occupancy).
+// in the padded x layout (single pass).
+//
+// Work is dealt as pairs (row j, virtual lane v).  With a multiple of 256
+// threads a thread keeps v = tid mod 256 and takes rows tid/256, tid/256 +
+// nt/256, ...; otherwise it takes v = tid, tid + nt, ... < 256 for every
+// row.  Either way the 64 lanes of a wave hold the 64 virtual lanes of one
+// group of one row, so the group's xor tree runs inside the wave.  The loads
+// of JB rows x CB chunks are issued together (at k <= 4096 and 8 waves: two
+// batches for m <= 2, where registers buy occupancy; one for m = 3, 4; two
+// for m > 4), g once per chunk for the JB rows when JB > 1.  The caller's
+// weight loads go out first: loads complete in issue order, and x / r / g
+// requested ahead of them delayed the weights more than it saved.
 template <int T, int M, bool TO_LDS>
 __device__ __forceinline__ void norm_partials(double *part, float *__restrict__ xs, uint32_t XS,
                                               const float *__restrict__ xb, const float *__restrict__ rb,
                                               const float *__restrict__ g, float *__restrict__ hb, uint32_t xrs,
                                               uint32_t k, uint32_t wave, uint32_t nwaves, uint32_t lane) {
+    constexpr int JB = M >= 4 ? 2 : 1;  // rows per batch
+    constexpr int CB = M <= 2 ? 2 : 4;  // chunks per row per batch (few rows: registers for occupancy)
     const uint32_t n4 = k >> 2;
-    for (uint32_t task = wave; task < 4u * M; task += nwaves) {
-        const uint32_t j = task >> 2, grp = task & 3;
-        double ss = 0.0;
-#pragma unroll 4
-        for (uint32_t q = grp * 64 + lane; q < n4; q += 256) {
-            const f32x4 xv = *(const f32x4 *)(xb + (uint64_t)j * xrs + 4 * q);
-            const f32x4 rv = *(const f32x4 *)(rb + (uint64_t)j * xrs + 4 * q);
-            f32x4 h;
+    const uint32_t nt = nwaves << 6, tid = (wave << 6) + lane;
+    const bool wide = (nt & 255u) == 0;
+    const uint32_t v_step = wide ? 256u : nt;
+    const uint32_t j_first = wide ? (tid >> 8) : 0u, j_step = wide ? (nt >> 8) : 1u;
+    const float *__restrict__ gg = TO_LDS ? g : nullptr;
+    for (uint32_t v = wide ? (tid & 255u) : tid; v < 256u; v += v_step) {
+        const uint32_t v0 = v & ~63u;  // the wave's first virtual lane (loop bounds stay wave-uniform)
+        for (uint32_t jb = j_first; jb < (uint32_t)M; jb += JB * j_step) {
+            double ss[JB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) h[i] = xv[i] + rv[i];
-            if (hb) *(f32x4 *)(hb + (uint64_t)j * xrs + 4 * q) = h;
-            if constexpr (TO_LDS) {
-                const uint32_t lv = 4 * q;
-                *(f32x4 *)(xs + j * XS + lv + 4 * (lv / Geo<T>::PADP)) = times_g(h, g, lv);
+            for (int i = 0; i < JB; ++i) ss[i] = 0.0;
+            for (uint32_t c0 = 0; v0 + 256u * c0 < n4; c0 += CB) {
+                // chunks q = v + 256 c, c = c0 .. c0 + CB - 1, of rows jb + i * j_step
+                f32x4 xv[JB][CB], rv[JB][CB], gv[CB];
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    const uint32_t q = v + 256u * (c0 + c);
+                    if (q < n4) {
+                        if (JB > 1 && gg) gv[c] = *(const f32x4 *)(gg + 4 * q);
+#pragma unroll
+                        for (int i = 0; i < JB; ++i) {
+                            const uint32_t j = jb + i * j_step;
+                            if (j < M) {
+                                xv[i][c] = *(const f32x4 *)(xb + (uint64_t)j * xrs + 4 * q);
+                                rv[i][c] = *(const f32x4 *)(rb + (uint64_t)j * xrs + 4 * q);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < CB; ++c) {
+                    const uint32_t q = v + 256u * (c0 + c);
+                    if (q < n4) {
+                        if (JB == 1 && gg) gv[c] = *(const f32x4 *)(gg + 4 * q);
+#pragma unroll
+                        for (int i = 0; i < JB; ++i) {
+                            const uint32_t j = jb + i * j_step;
+                            if (j < M) {
+                                f32x4 h;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) h[e] = xv[i][c][e] + rv[i][c][e];
+                                if (hb) *(f32x4 *)(hb + (uint64_t)j * xrs + 4 * q) = h;
+                                if constexpr (TO_LDS) {
+                                    const uint32_t lv = 4 * q;
+                                    f32x4 u = h;
+                                    if (gg) {
+#pragma unroll
+                                        for (int e = 0; e < 4; ++e) u[e] = h[e] * gv[c][e];
+                                    }
+                                    *(f32x4 *)(xs + j * XS + lv + 4 * (lv / Geo<T>::PADP)) = u;
+                                }
+                                ss[i] = fold4(ss[i], h);
+                            }
+                        }
+                    }
+                }
             }
-            ss = fold4(ss, h);
-        }
 #pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) ss += shfl_xor_d(ss, msk);
-        if (lane == 0) part[task] = ss;
+            for (int msk = 32; msk >= 1; msk >>= 1) {
+#pragma unroll
+                for (int i = 0; i < JB; ++i) ss[i] += shfl_xor_d(ss[i], msk);
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < JB; ++i) {
+                    const uint32_t j = jb + i * j_step;
+                    if (j < M) part[4 * j + (v >> 6)] = ss[i];
+                }
+            }
+        }
     }
 }
 
@@ -920,10 +981,10 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 }
             }
         };
-        prefetch(A);
-        if (DEPTH == 2) prefetch(B);
         double *part = (double *)((uint8_t *)xs + a.norm_offset);
         const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
+        prefetch(A);
+        if (DEPTH == 2) prefetch(B);
         if constexpr (NORM)
             norm_partials<T, M, true>(part, xs, XS, xb, a.r + b * a.xbs, a.g,
                                       (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);

@@ -111,3 +111,27 @@ def test_add_rmsnorm_multipass_matches_single_pass():
         _, y1 = _run(t, Wd, xd[j * k:], rd[j * k:], gd, 1e-5, n, k, 1)
         assert np.array_equal(bits(y1), y8b[j]), f"row {j}: multi-pass m=8 differs from single-pass m=1"
     assert np.array_equal(h8.cpu().numpy(), (x + r).ravel())
+
+
+@pytest.mark.parametrize("t,n,k", [(wl.Q8_0, 2048, 4160), (wl.F16, 4096, 1028), (wl.Q6_K, 2048, 14336)],
+                         ids=["q8_0-single-pass", "f16-short-rows", "q6_k-multi-pass"])
+def test_add_rmsnorm_full_workgroups(t, n, k):
+    """Enough rows for workgroups of 4 and 8 waves, where a thread keeps one
+    virtual lane of the statistic and takes several input rows: every m
+    within tolerance, h bit-exact, each row bitwise equal to its m = 1 run."""
+    W = wl.weights(t, n, k, seed=1500 + t)
+    x = wl.activations(8, k, seed=1501)
+    r = wl.activations(8, k, seed=1502)
+    g = (1.0 + 0.1 * wl.activations(1, k, seed=1503)[0]).astype(np.float32)
+    Wd, xd, rd, gd = to_dev(W.ravel()), to_dev(x.ravel()), to_dev(r.ravel()), to_dev(g)
+    waves = {qfr.row_exact_schedule(t, n, k, m).waves_per_workgroup for m in range(1, 9)}
+    assert waves & {4, 8}, waves
+    _, _, yref, a = oracle.mv_add_rmsnorm(t, W, x, r, g, 1e-5, n, k, 8)
+    y1 = [bits(_run(t, Wd, xd[j * k:], rd[j * k:], gd, 1e-5, n, k, 1)[1]) for j in range(8)]
+    for m in range(1, 9):
+        h, y = _run(t, Wd, xd, rd, gd, 1e-5, n, k, m)
+        check_tolerance(y.cpu().numpy().reshape(1, m, n), yref[:, :m], a[:, :m], f"m={m}")
+        assert np.array_equal(h.cpu().numpy(), (x[:m] + r[:m]).ravel()), f"m={m}: h"
+        yb = bits(y).reshape(m, n)
+        for j in range(m):
+            assert np.array_equal(yb[j], y1[j]), f"m={m} row {j} differs from its m = 1 run"
