@@ -14,6 +14,13 @@
 #include "re_internal.h"
 #include "row_exact_mv.h"
 
+// Waves with at least this many items walk with unconditional loads (more
+// than the load depth of 2; measured on MI355X: waves of one or two items are
+// faster with the loads under a branch).
+#ifndef REX_WALK_UNCONDITIONAL_MIN_ITEMS
+#define REX_WALK_UNCONDITIONAL_MIN_ITEMS 3
+#endif
+
 using namespace rex;
 
 namespace {
@@ -463,6 +470,13 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     a.h = norm ? norm->h : nullptr;
     a.eps = norm ? norm->eps : 0.0f;
     a.norm_offset = (uint32_t)lds_x_bytes(t, m, k, sch.k_chunk);
+    {
+        // items a wave walks in the single pass: its row groups x wave steps
+        const uint32_t waves = sch.waves_per_workgroup;
+        const uint64_t steps = (a.pieces + (1u << a.lpr_log2) - 1) >> a.lpr_log2;
+        const uint64_t items = (uint64_t)((a.groups_per_wg + waves - 1) / waves) * steps;
+        a.walk_unconditional = items >= REX_WALK_UNCONDITIONAL_MIN_ITEMS ? 1u : 0u;
+    }
     const uint64_t grid_x = (uint64_t)wgs * batch;
     if (grid_x > 0x7fffffffull)
         return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);

@@ -37,6 +37,7 @@ struct MvArgs {
     float *h;
     float eps;
     uint32_t norm_offset;       // byte offset in LDS of the m per-row inverse RMS values (double)
+    uint32_t walk_unconditional;  // 1: waves hold more items than the load depth (see fetch_item)
 };
 
 struct DqArgs {

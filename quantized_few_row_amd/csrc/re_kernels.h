@@ -49,6 +49,9 @@
 #ifndef REX_DEPTH_BUDGET
 #define REX_DEPTH_BUDGET 120
 #endif
+#ifndef REX_X_FIRST_MAX_M
+#define REX_X_FIRST_MAX_M 2
+#endif
 
 
 namespace rex {
@@ -547,6 +550,7 @@ __device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *_
 
 // ---------------------------------------------------------------- x staging
 
+// Stage values [v0, v1) of the m input rows into LDS.
 template <int T, int M>
 __device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
                                         uint32_t v0, uint32_t v1, uint32_t XS) {
@@ -574,6 +578,46 @@ __device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__r
                 for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = v[u][j];
             }
         }
+    }
+}
+
+// The same for few input rows, with `between` run once after the first
+// batch of loads is issued and before any of it is written to LDS (the
+// caller issues its first weight loads there): x is then a few loads per
+// thread that arrive well before the weights, and the barrier after the
+// staging does not wait for every wave's weights.
+template <int T, int M, typename F>
+__device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
+                                              uint32_t k, uint32_t XS, F &&between) {
+    constexpr int U = M >= 2 ? 1 : 2;  // k = 4096 at 512 threads: one batch
+    const uint32_t n4 = k >> 2;
+    const uint32_t nt = blockDim.x;
+    f32x4 v[U][M];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t q = threadIdx.x + u * nt;
+        if (q < n4) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) v[u][j] = *(const f32x4 *)(xb + (uint64_t)j * xrs + 4 * q);
+        }
+    }
+    between();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t q = threadIdx.x + u * nt;
+        if (q < n4) {
+            const uint32_t lv = 4 * q;
+            const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+#pragma unroll
+            for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = v[u][j];
+        }
+    }
+    // the rest (k > 4 U nt), behind the weights
+    for (uint32_t q = threadIdx.x + U * nt; q < n4; q += nt) {
+        const uint32_t lv = 4 * q;
+        const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+#pragma unroll
+        for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = *(const f32x4 *)(xb + (uint64_t)j * xrs + lv);
     }
 }
 
@@ -899,26 +943,42 @@ template <int T, int M, int NR> struct Depth {
     static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= REX_DEPTH_BUDGET) ? 2 : 1;
 };
 
+// Loads the item at the load cursor (lg, ls) into dst and advances the
+// cursor.  UNC: the loads are issued even past the wave's last item (then
+// every lane reads piece 0 of the workgroup's last group, one line), so the
+// code is straight-line and the compiler's wait before a multiply covers
+// exactly the item being multiplied; with the loads under a branch it has to
+// assume either path and waits for the items still in flight as well.  The
+// branch form is kept for waves with at most DEPTH items, where the extra
+// loads would cost more than the waits.
+template <int T, int NR, bool SUB, bool UNC>
+__device__ __forceinline__ void fetch_item(const uint8_t *__restrict__ Wb, const MvArgs &a, uint32_t &lg, uint32_t &ls,
+                                           uint32_t g1, uint32_t gstride, uint32_t S, uint32_t li, uint32_t slot,
+                                           typename Tr<T>::Raw (&dst)[NR]) {
+    const bool have = lg < g1;
+    if (UNC || have)
+        load_item<T, NR, SUB>(Wb, a, have ? lg : g1 - 1,
+                              have ? min((ls << lpr_of<SUB>(a)) + li, a.pieces - 1) : 0u, slot, dst);
+    if (have && ++ls == S) {
+        ls = 0;
+        lg += gstride;
+    }
+}
+
 // One step of the single-pass walk.  Items are (row group g, step s):
 // pieces L*s + li of the group's rows, for the lane's index li < L in its
 // row slot (L lanes per row; L = 64: one slot of NR rows).  The load cursor (lg, ls) runs
 // DEPTH items ahead of the compute cursor (cg, cs): the step loads the item
 // at the load cursor into `nxt`, multiplies `cur`, and stores a group's
 // outputs after its last step.  Returns whether items remain.
-template <int T, int M, int NR, bool SUB>
+template <int T, int M, int NR, bool SUB, bool UNC>
 __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__restrict__ Wb, float *__restrict__ yb,
                                           const float *__restrict__ xs, uint32_t XS, uint32_t &lg, uint32_t &ls,
                                           uint32_t &cg, uint32_t &cs, uint32_t gstride, uint32_t g1, uint32_t S,
                                           uint32_t lane, uint32_t li, uint32_t slot, const RowScale &sc,
                                           const typename Tr<T>::Raw (&cur)[NR], typename Tr<T>::Raw (&nxt)[NR],
                                           float (&acc)[NR][M]) {
-    if (lg < g1) {
-        load_item<T, NR, SUB>(Wb, a, lg, min((ls << lpr_of<SUB>(a)) + li, a.pieces - 1), slot, nxt);
-        if (++ls == S) {
-            ls = 0;
-            lg += gstride;
-        }
-    }
+    fetch_item<T, NR, SUB, UNC>(Wb, a, lg, ls, g1, gstride, S, li, slot, nxt);
     const uint32_t pc = (cs << lpr_of<SUB>(a)) + li;
     if (pc < a.pieces) compute_piece<T, M, NR>(acc, cur, pc, 0, xs, XS, a.k);
     if (cs == S - 1) {
@@ -938,7 +998,7 @@ __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__rest
 // the others have 64 lanes per row as compile-time constants.  NORM: the
 // instances with the fused add + RMS normalisation (a.r != NULL); kept apart
 // so that its prologue's registers do not cost the plain product occupancy.
-template <int T, int M, int NR, bool SUB, bool NORM>
+template <int T, int M, int NR, bool SUB, bool NORM, bool UNC>
 __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     extern __shared__ float xs[];
     const uint32_t lane = threadIdx.x & 63u;
@@ -981,37 +1041,43 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         uint32_t lg = g0 + wave, ls = 0;
         const uint32_t gfirst = lg;
         Raw A[NR], B[NR], C[NR];
-        auto prefetch = [&](Raw(&dst)[NR]) {
-            if (lg < g1) {
-                load_item<T, NR, SUB>(Wb, a, lg, min((ls << lpr) + li, a.pieces - 1), slot, dst);
-                if (++ls == S) {
-                    ls = 0;
-                    lg += nwaves;
-                }
-            }
-        };
         double *part = (double *)((uint8_t *)xs + a.norm_offset);
         const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
-        prefetch(A);
-        if (DEPTH == 2) prefetch(B);
-        if constexpr (NORM)
+        // The first DEPTH items' loads: straight-line (see fetch_item) for
+        // the unconditional walk and for x staged ahead of them (so that the
+        // x loads can be waited for without them); under a branch otherwise
+        // (measured faster for waves of one or two items at m >= 3).
+        constexpr bool UP = UNC || M <= REX_X_FIRST_MAX_M;
+        auto prefetch_first = [&] {
+            fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, A);
+            if (DEPTH == 2) fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, B);
+        };
+        if constexpr (NORM) {
+            prefetch_first();
             norm_partials<T, M, true>(part, xs, XS, xb, a.r + b * a.xbs, a.g,
                                       (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);
-        else
+        } else if constexpr (M <= REX_X_FIRST_MAX_M) {
+            // few input rows: x is a few loads per thread, requested ahead of
+            // the weights, so the barrier does not wait for every wave's weights
+            stage_x_first<T, M>(xs, xb, a.xrs, a.k, XS, prefetch_first);
+        } else {
+            prefetch_first();
             stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
+        }
         __syncthreads();
         if (gfirst < g1) {
+            constexpr bool U = UNC;
             float acc[NR][M];
             zero<M, NR>(acc);
             uint32_t cg = gfirst, cs = 0;
             if constexpr (DEPTH == 2) {
-                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, A, C, acc) &&
-                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, B, A, acc) &&
-                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, C, B, acc)) {
+                while (walk_step<T, M, NR, SUB, U>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, A, C, acc) &&
+                       walk_step<T, M, NR, SUB, U>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, B, A, acc) &&
+                       walk_step<T, M, NR, SUB, U>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, C, B, acc)) {
                 }
             } else {
-                while (walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, A, B, acc) &&
-                       walk_step<T, M, NR, SUB>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, B, A, acc)) {
+                while (walk_step<T, M, NR, SUB, U>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, A, B, acc) &&
+                       walk_step<T, M, NR, SUB, U>(a, Wb, yb, xs, XS, lg, ls, cg, cs, nwaves, g1, S, lane, li, slot, sc, B, A, acc)) {
                 }
             }
         }
@@ -1078,10 +1144,13 @@ __global__ void __launch_bounds__(256) dq_kernel(const DqArgs a) {
 
 template <int T, int M, int NR>
 hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    const void *fn = a.lpr_log2 < 6 ? (a.r ? (const void *)mv_kernel<T, M, NR, true, true>
-                                           : (const void *)mv_kernel<T, M, NR, true, false>)
-                                    : (a.r ? (const void *)mv_kernel<T, M, NR, false, true>
-                                           : (const void *)mv_kernel<T, M, NR, false, false>);
+    // Unconditional-load walks (see fetch_item) only for the plain 64-lane
+    // instances, where waves hold many items on the large shapes.
+    const void *fn = a.lpr_log2 < 6 ? (a.r ? (const void *)mv_kernel<T, M, NR, true, true, false>
+                                           : (const void *)mv_kernel<T, M, NR, true, false, false>)
+                   : a.r            ? (const void *)mv_kernel<T, M, NR, false, true, false>
+                   : a.walk_unconditional ? (const void *)mv_kernel<T, M, NR, false, false, true>
+                                          : (const void *)mv_kernel<T, M, NR, false, false, false>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -1093,7 +1162,7 @@ hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStr
 
 template <int T, int M, int NR>
 hipError_t attributes_one(hipFuncAttributes *attr) {
-    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR, false, false>);
+    return hipFuncGetAttributes(attr, (const void *)mv_kernel<T, M, NR, false, false, false>);
 }
 
 template <int T, int M>
