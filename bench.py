@@ -26,6 +26,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,6 +57,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only run a plain device copy of this many MiB, --steps times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write profiles/traffic.json from four rocprofv3 --pmc csv output folders: FETCH_SIZE and "
+                         "WRITE_SIZE of a --profile-only run, then of a --copy-calibration run of the size given "
+                         "with --copy-calibration (no GPU needed)")
     return ap.parse_args()
 
 
@@ -85,8 +90,78 @@ def measured_traffic(workload, m):
     return None if ent is None else ent.get("hbm_bytes")
 
 
+def _counter_rows(folder, counter):
+    """(kernel name, value) of every dispatch in the rocprofv3 csv files under folder."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"bench.py: no {counter} rows under {folder}")
+    return rows
+
+
+def copy_calibration_bytes(mib):
+    """Bytes the --copy-calibration run copies per launch."""
+    return int(mib * (1 << 20)) // 16 * 16
+
+
+def write_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes, workload="q8_0_4096x4096"):
+    """HBM bytes per launch of the mat-vec kernels from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for a plain
+    device copy of known size (``--copy-calibration``), into profiles/traffic.json."""
+    import statistics
+
+    import workloads as wl
+    def cal_factor(folder, counter):
+        rows = _counter_rows(folder, counter)
+        copies = [v for name, v in rows if "copy" in name.lower()]
+        if not copies:  # the kernel launched most often is the copy
+            names = [name for name, _ in rows]
+            top = max(set(names), key=names.count)
+            copies = [v for name, v in rows if name == top]
+        return statistics.median(copies)
+    fetch_factor = cal_factor(cal_fetch_dir, "FETCH_SIZE") * 1024 / cal_bytes
+    write_factor = cal_factor(cal_write_dir, "WRITE_SIZE") * 1024 / cal_bytes
+    w = wl.get(workload)
+    launches = {}
+    per = {}
+    for folder, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for name, v in _counter_rows(folder, counter):
+            mt = re.search(r"mv_kernel<\s*(\d+)\s*,\s*(\d+)", name)
+            if mt:
+                per.setdefault((int(mt.group(2)), counter), []).append(v)
+    import quantized_few_row_amd as qfr
+    xrs, xbs, yrs, ybs = w.strides(8)
+    s = qfr.Strides(xrs, xbs, yrs, ybs)
+    for m in sorted({m for m, _ in per}):
+        fk = statistics.mean(per[(m, "FETCH_SIZE")])
+        wk = statistics.mean(per[(m, "WRITE_SIZE")])
+        fb, wb = fk * 1024 / fetch_factor, wk * 1024 / write_factor
+        _, xb, yb = qfr.row_exact_required_bytes(w.wtype, w.n, w.k, m, w.batch, s)
+        launches[f"{workload}:m{m}"] = {
+            "hbm_bytes": int(round(fb + wb)), "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
+            "fetch_size_kib": fk, "write_size_kib": wk, "dispatches": len(per[(m, "FETCH_SIZE")]),
+            "algorithmic_bytes": w.weight_bytes + xb + yb}
+    rec = {"kernel_source_hash": kernel_source_hash(),
+           "copy_calibration": {"bytes": cal_bytes, "fetch_factor": fetch_factor, "write_factor": write_factor},
+           "launches": launches}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        if not args.copy_calibration:
+            raise SystemExit("bench.py: --write-traffic needs --copy-calibration MIB (the size of the calibration copy)")
+        write_traffic(*args.write_traffic, copy_calibration_bytes(args.copy_calibration))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the mat-vec shards by weight rows with no "
               "reduction, and multi-GPU runs are not part of it (use --gpus 1).", file=sys.stderr)
@@ -101,7 +176,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration:
-        nbytes = int(args.copy_calibration * (1 << 20)) // 16 * 16
+        nbytes = copy_calibration_bytes(args.copy_calibration)
         a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(args.steps):
