@@ -263,7 +263,11 @@ uint32_t max_rows_per_wave(int t, uint32_t m) {
     return 4;
 }
 
-int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, row_exact_schedule_t &s) {
+// fused_norm: the schedule of row_exact_mv_add_rmsnorm (its instances carry
+// the normalisation prologue; rows per wave as before the single-row rule
+// below, which measured 3% slower there at m = 4).
+int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, row_exact_schedule_t &s,
+                     bool fused_norm = false) {
     DevInfo di;
     int rc = device_info(di);
     if (rc) return rc;
@@ -281,10 +285,22 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         // Few input rows: the weight loads dominate.  Measured best on
         // MI355X: about 32 waves per CU over the whole grid (the hardware
         // balances the tail across workgroups), one row group per wave while
-        // the rows allow it, single rows beyond that.
-        const uint64_t target = (uint64_t)di.cus * 32;
-        const uint64_t wave_rows = rows >> (6 - lanes_per_row_log2(t, k));  // rows / slots per wave
-        const uint32_t nr = (wave_rows > target && wave_rows <= 2 * target) ? 2u : 1u;
+        // the rows allow it, single rows beyond that.  A row group of a
+        // single wave step is one item, and a wave with one item has nothing
+        // to multiply while its loads are in flight: rows of one step take
+        // single rows on 24 waves per CU instead, so each wave walks two or
+        // more of them (Q4_K 14336 x 4096: 12.3 -> 10.8 us at m = 1).
+        uint64_t target = (uint64_t)di.cus * 32;
+        const uint32_t lpr = lanes_per_row_log2(t, k);
+        const uint64_t wave_rows = rows >> (6 - lpr);  // rows / slots per wave
+        const uint32_t steps = (pieces_of(t, k) + (1u << lpr) - 1) >> lpr;
+        uint32_t nr = 1;
+        if (wave_rows > target && wave_rows <= 2 * target) {
+            if (steps >= 2)
+                nr = 2;
+            else
+                target = (uint64_t)di.cus * 24;
+        }
         s.rows_per_wave = nr;
         const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
         const uint32_t gpb = (n + rg - 1) / rg;
@@ -299,8 +315,18 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     }
     // rows per wave: the most that still leaves 8 waves per CU
     const uint64_t target_waves = (uint64_t)di.cus * 8;
+    const uint32_t lpr = lanes_per_row_log2(t, k);
+    const uint64_t wave_rows = rows >> (6 - lpr);
     uint32_t nr = max_rows_per_wave(t, m);
-    while (nr > 1 && (rows >> (6 - lanes_per_row_log2(t, k))) / nr < target_waves) nr >>= 1;
+    while (nr > 1 && wave_rows / nr < target_waves) nr >>= 1;
+    // Up to 4 input rows and fewer than 16 rows per wave: single rows, so
+    // each wave walks more items with loads in flight behind the multiply
+    // (measured 3-18% faster than 2 or 4 rows per wave at m = 2..4 on
+    // 4096 x 4096 Q8_0, BF16, F32, 14336 x 4096 Q4_K and 16 x 1024 x 4096
+    // Q5_0; the 128256-row head keeps 4).  Short rows (a wave already
+    // covers 2 or 4 rows per item) and the fused-norm instances measured
+    // slower with it and keep the rule above.
+    if (m <= 4 && kc >= k && lpr == 6 && !fused_norm && wave_rows < 16 * target_waves) nr = 1;
     s.rows_per_wave = nr;
     const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
     const uint32_t gpb = (n + rg - 1) / rg;
@@ -314,7 +340,14 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     uint32_t wgs;
     if (kc >= k) {
         const int per_cu = workgroups_per_cu(t, m, nr, waves, lds_bytes(t, m, k, kc), di.lds_max);
-        const uint64_t target = (uint64_t)di.cus * (uint64_t)per_cu;
+        uint64_t target = (uint64_t)di.cus * (uint64_t)per_cu;
+        // Each workgroup stages m*k*4 bytes of x from L2: fewer workgroups
+        // (whole rounds of the device) when more would stream fewer weight
+        // bytes each than they stage (Q8_0 4096 x 4096 at m = 4: one
+        // workgroup per CU, 8.7 -> 8.2 us).
+        const uint64_t x_wg = (uint64_t)m * k * sizeof(float);
+        const u128 by_x = (u128)rows * row_bytes_of(t, k) / x_wg / di.cus * di.cus;
+        if (by_x < target) target = by_x > di.cus ? (uint64_t)by_x : (uint64_t)di.cus;
         uint64_t w = (target + batch - 1) / batch;
         if (w < 1) w = 1;
         wgs = (uint32_t)(w < max_wgs ? w : max_wgs);
@@ -425,7 +458,7 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     if (pin) {
         sch = *pin;
     } else {
-        rc = default_schedule(t, n, k, m, batch, sch);
+        rc = default_schedule(t, n, k, m, batch, sch, norm != nullptr);
         if (rc) return rc;
     }
     rc = check_schedule_fields(t, k, sch);
