@@ -126,8 +126,18 @@ size_t lds_x_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
     const uint32_t kc = k_chunk < k ? k_chunk : k;
     return (size_t)m * xs_stride(t, kc) * sizeof(float);
 }
-size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
+// Floats per input row of the segment sums (Q4_K: one per 32 staged values).
+uint32_t sx_stride(int t, uint32_t k, uint32_t k_chunk) {
+    const uint32_t kc = k_chunk < k ? k_chunk : k;
+    return t == kQ4K ? kc / 32 : 0;
+}
+// LDS layout: staged x (m rows, padded), 4 m doubles of the fused norm's
+// statistic, the segment sums (m rows).
+size_t lds_sx_offset(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
     return lds_x_bytes(t, m, k, k_chunk) + (size_t)4 * m * sizeof(double);
+}
+size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
+    return lds_sx_offset(t, m, k, k_chunk) + (size_t)m * sx_stride(t, k, k_chunk) * sizeof(float);
 }
 
 typedef unsigned __int128 u128;
@@ -503,6 +513,8 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     a.h = norm ? norm->h : nullptr;
     a.eps = norm ? norm->eps : 0.0f;
     a.norm_offset = (uint32_t)lds_x_bytes(t, m, k, sch.k_chunk);
+    a.sx_offset = (uint32_t)lds_sx_offset(t, m, k, sch.k_chunk);
+    a.sx_stride = sx_stride(t, k, sch.k_chunk);
     {
         // items a wave walks in the single pass: its row groups x wave steps
         const uint32_t waves = sch.waves_per_workgroup;

@@ -5,9 +5,10 @@
 //
 // Work decomposition
 //   - A weight row is cut into "pieces": per-lane work items whose bytes sit
-//     together in the row (F16: 8 values; Q8_0 / Q5_0: one block; Q4_K: 16
-//     nibble bytes of a super-block; Q6_K: a quarter super-block).  Lane L of
-//     the wave owning the row takes pieces L, L+64, L+128, ... in that order,
+//     together in the row (F16: 8 values; Q8_0 / Q5_0: one block; Q4_K: 32
+//     nibble bytes, two sub-blocks, of a super-block; Q6_K: a quarter
+//     super-block).  Lane L of the wave owning the row takes pieces L, L+64,
+//     L+128, ... in that order,
 //     so each load instruction of a wave covers adjacent bytes of the row.
 //   - A wave streams rows_per_wave (NR) rows at once: every input value read
 //     from LDS feeds NR weight rows ("nr0 rows sharing each input load").
@@ -15,17 +16,20 @@
 //     (padded so that the lanes' 16-byte reads hit distinct banks).
 //
 // Numerics (module docs, "Row exactness")
-//   - Every weight is decoded exactly in registers.  F16 and Q4_K weights are
-//     decoded to their float32 value w (Q4_K's is one rounding of an exact
-//     difference, via fma).  Q8_0, Q5_0 and Q6_K weights are s * q with an
-//     integer-valued q and a scale s shared by a segment of values (a block;
-//     16 values for Q6_K): they are decoded to q, exactly.
+//   - Every weight is decoded exactly in registers.  Dense weights (F16,
+//     BF16, F32) are decoded to their float32 value w.  Q8_0, Q5_0 and Q6_K
+//     weights are s * q with an integer-valued q and a scale s shared by a
+//     segment of values (a block; 16 values for Q6_K); Q4_K weights are
+//     s * q - o with a scale and an offset shared by a 32-value sub-block:
+//     they are decoded to q, exactly.
 //   - For each (row, input row) a lane keeps one accumulator and folds its
 //     pieces into it with an explicit fmaf chain, in piece order and, inside
 //     a piece, in a fixed value order: acc = fma(w, x, acc) per value, or,
-//     per scaled segment, part = q*x then fma(q, x, part) over its values and
-//     acc = fma(s, part, acc).  Nothing about those chains depends on m or on
-//     the packing (NR, waves per workgroup, grid).
+//     per scaled segment, part = q*x then fma(q, x, part) over its values,
+//     acc = fma(s, part, acc) and, for Q4_K, acc = fma(-o, sum_x, acc) with
+//     the segment's sum of x, which each workgroup forms once per input row
+//     in a fixed order.  Nothing about those chains depends on m or on the
+//     packing (NR, waves per workgroup, grid).
 //   - The 64 lane partials of an output are added by one fixed tree: lanes
 //     (L, L^32), then (L, L^16), then within each row of 16 lanes: rotate-8,
 //     half-row mirror, xor 2, xor 1.  The first two levels are done with the
@@ -63,6 +67,7 @@ typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32x4a2 __attribute__((ext_vector_type(4), aligned(2)));
 typedef uint32_t u32x2a2 __attribute__((ext_vector_type(2), aligned(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Exact widening of an IEEE half (subnormals included).
 __device__ __forceinline__ float h2f(uint32_t bits) {
@@ -302,7 +307,9 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
 // values 64c + 32..63 of sub-block 2c+1.
 // w = fma(d*sc, q, -(dmin*mn)): one rounding of the exact value.
 template <> struct Tr<kQ4K> : Geo<kQ4K> {
-    static constexpr int SEG = 0;  // w = d*sc*q - dmin*mn is formed per value (the offset does not factor)
+    // One scale and one offset per 32 values (groups 8e..8e+7, sub-block
+    // 2c+e): the segment contributes d*sc * sum(q*x) - dmin*mn * sum(x).
+    static constexpr int SEG = 8;
     struct Raw { uint32_t qs[8]; uint32_t h[4]; };
     struct Pre { float dsc[2], dmn[2]; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -343,6 +350,16 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(pr.dsc[e], (float)((q4 >> (8 * i)) & 0xffu), -pr.dmn[e]);
     }
+    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+        const uint32_t dw = r.qs[g & 7];
+        const uint32_t q4 = opaque(g >= 8 ? ((dw >> 4) & 0x0F0F0F0Fu) : (dw & 0x0F0F0F0Fu));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = (float)((q4 >> (8 * i)) & 0xffu);
+    }
+    static __device__ __forceinline__ float scale(const Pre &pr, int e) { return pr.dsc[e]; }
+    static __device__ __forceinline__ float offset(const Pre &pr, int e) { return pr.dmn[e]; }
+    // index of the piece's first segment among the pass's segment sums
+    static __device__ __forceinline__ uint32_t sxoff(uint32_t p, uint32_t vb) { return 2 * p - vb / 32; }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) {
         return 256 * (p >> 2) + 64 * (p & 3) + (g >= 8 ? 32 : 0) + 4 * (g & 7);
     }
@@ -621,6 +638,30 @@ __device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const floa
     }
 }
 
+// Segment sums of the staged input (offset types): sx[j*SXS + s] = the sum
+// of staged values 32s .. 32s+31 of input row j by one fixed pairwise tree
+// (each 4 values as (a+b)+(c+d), then the 8 sums pairwise, in order), the
+// same steps for every m and every packing.  Needs the staged values
+// written (a barrier) and a barrier before use.
+template <int T, int M>
+__device__ __forceinline__ void stage_sx(const float *__restrict__ xs, uint32_t XS, float *__restrict__ sx,
+                                         uint32_t SXS, uint32_t nvals) {
+    static_assert(Geo<T>::PADP % 32 == 0, "a segment must not straddle a pad");
+    const uint32_t nseg = nvals / 32;
+    for (uint32_t i = threadIdx.x; i < M * nseg; i += blockDim.x) {
+        const uint32_t j = i / nseg, sg = i - j * nseg;
+        const uint32_t lv = 32 * sg;
+        const float *__restrict__ src = xs + j * XS + lv + 4 * (lv / Geo<T>::PADP);
+        f32x4 v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = *(const f32x4 *)(src + 4 * c);
+        float t[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) t[c] = (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
+        sx[j * SXS + sg] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    }
+}
+
 // ---------------------------------------------------------------- fused add + RMS norm
 //
 // nuvec-core 0.6.0, src/gpu.rs, add_rms_norm (FastOp::AddRmsNorm): the sum
@@ -783,9 +824,14 @@ __device__ __forceinline__ void stage_u(float *__restrict__ xs, const float *__r
 
 // ---------------------------------------------------------------- one piece
 
+// Types whose segments carry an offset term (- offset * sum of the
+// segment's x) besides the scale.
+template <int T> constexpr bool kOffsets = T == kQ4K;
+
 template <int T, int M, int NR>
 __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typename Tr<T>::Raw (&raw)[NR], uint32_t p,
-                                              uint32_t vb, const float *__restrict__ xs, uint32_t XS, uint32_t k) {
+                                              uint32_t vb, const float *__restrict__ xs, uint32_t XS, uint32_t k,
+                                              const float *__restrict__ sx, uint32_t SXS) {
     using TR = Tr<T>;
     typename TR::Pre pre[NR];
 #pragma unroll
@@ -820,6 +866,12 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
 #pragma unroll
         for (int j = 0; j < M; ++j) xv[0][j] = *(const f32x4 *)(xp + j * XS + TR::goff(0));
         float part[NR][M];
+        // the sums of x over the piece's two segments (offset types)
+        f32x2 sv[M];
+        if constexpr (kOffsets<T>) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) sv[j] = *(const f32x2 *)(sx + j * SXS + TR::sxoff(p, vb));
+        }
 #pragma unroll
         for (int g = 0; g < TR::NG; ++g) {
             const int gg = g % TR::SEG, cb = g & 1;
@@ -845,6 +897,11 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
                     const float sc = TR::scale(pre[r], g / TR::SEG);
 #pragma unroll
                     for (int j = 0; j < M; ++j) acc[r][j] = __builtin_fmaf(sc, part[r][j], acc[r][j]);
+                    if constexpr (kOffsets<T>) {
+                        const float of = TR::offset(pre[r], g / TR::SEG);
+#pragma unroll
+                        for (int j = 0; j < M; ++j) acc[r][j] = __builtin_fmaf(-of, sv[j][g / TR::SEG], acc[r][j]);
+                    }
                 }
             }
             if (M >= REX_SCHED_BARRIER_MIN_M) __builtin_amdgcn_sched_barrier(0);
@@ -857,7 +914,8 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
 template <int T, int M, int NR>
 __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *const (&R)[NR],
                                            const uint32_t (&o0)[NR], uint32_t pb, uint32_t pe, uint32_t vb,
-                                           const float *__restrict__ xs, uint32_t XS, uint32_t k, uint32_t lane) {
+                                           const float *__restrict__ xs, uint32_t XS, uint32_t k, uint32_t lane,
+                                           const float *__restrict__ sx, uint32_t SXS) {
     using TR = Tr<T>;
     using Raw = typename TR::Raw;
     uint32_t p = pb + lane;
@@ -870,13 +928,13 @@ __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *c
         const bool m1 = p1 < pe;
 #pragma unroll
         for (int r = 0; r < NR; ++r) B[r] = TR::load(R[r], o0[r], m1 ? p1 : p, k);
-        compute_piece<T, M, NR>(acc, A, p, vb, xs, XS, k);
+        compute_piece<T, M, NR>(acc, A, p, vb, xs, XS, k, sx, SXS);
         if (!m1) break;
         const uint32_t p2 = p1 + 64;
         const bool m2 = p2 < pe;
 #pragma unroll
         for (int r = 0; r < NR; ++r) A[r] = TR::load(R[r], o0[r], m2 ? p2 : p1, k);
-        compute_piece<T, M, NR>(acc, B, p1, vb, xs, XS, k);
+        compute_piece<T, M, NR>(acc, B, p1, vb, xs, XS, k, sx, SXS);
         if (!m2) break;
         p = p2;
     }
@@ -980,7 +1038,9 @@ __device__ __forceinline__ bool walk_step(const MvArgs &a, const uint8_t *__rest
                                           float (&acc)[NR][M]) {
     fetch_item<T, NR, SUB, UNC>(Wb, a, lg, ls, g1, gstride, S, li, slot, nxt);
     const uint32_t pc = (cs << lpr_of<SUB>(a)) + li;
-    if (pc < a.pieces) compute_piece<T, M, NR>(acc, cur, pc, 0, xs, XS, a.k);
+    if (pc < a.pieces)
+        compute_piece<T, M, NR>(acc, cur, pc, 0, xs, XS, a.k, (const float *)((const uint8_t *)xs + a.sx_offset),
+                                a.sx_stride);
     if (cs == S - 1) {
         store_group<M, NR, SUB>(a, acc, yb, cg, lane, sc);
         zero<M, NR>(acc);
@@ -1065,6 +1125,10 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
         }
         __syncthreads();
+        if constexpr (kOffsets<T>) {
+            stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, a.k);
+            __syncthreads();
+        }
         if (gfirst < g1) {
             constexpr bool U = UNC;
             float acc[NR][M];
@@ -1110,7 +1174,13 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 else
                     stage_x<T, M>(xs, xb, a.xrs, vb, ve, XS);
                 __syncthreads();
-                if (active) accumulate<T, M, NR>(acc, R, o0, pb, pe, vb, xs, XS, a.k, lane);
+                if constexpr (kOffsets<T>) {
+                    stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, ve - vb);
+                    __syncthreads();
+                }
+                if (active)
+                    accumulate<T, M, NR>(acc, R, o0, pb, pe, vb, xs, XS, a.k, lane,
+                                         (const float *)((const uint8_t *)xs + a.sx_offset), a.sx_stride);
             }
             if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane, sc);
         }
