@@ -367,6 +367,10 @@ def main():
             "kernel": f"mv_kernel<{wl.TYPE_NAMES[t]}, m={dom}>",
             "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload, dom),
+            "peak_basis": ("unpacked FP32 FMA: 256 CUs x 64 lanes x 2 flops x 2.4 GHz (packed FP32 is "
+                           "disabled in this build; the published 157.3 TFLOP/s counts two FMAs per lane)"
+                           if bound == "alu" else "MI355X HBM3E, 8 TB/s"),
+            "frac_of_published_fp32": (round(achieved / 157.3, 4) if bound == "alu" else None),
             "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops[dom],
             "mean_launch_us": round(kernel_us[dom], 3),
         },

@@ -379,32 +379,44 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
 // w = (d * sc) * (q - 32), exact.
 template <> struct Tr<kQ6K> : Geo<kQ6K> {
     static constexpr int SEG = 4;  // one scale per 16 values (groups 4t..4t+3)
-    struct Raw { uint32_t ql0[4], ql1[4], qhx[4], sc[2], d; };
+    // s4: the piece's four sub-scales sc[8hh + 2t + l0/16], t = 0..3, as bytes 0..3.
+    struct Raw { uint32_t ql0[4], ql1[4], qhx[4], s4, d; };
     struct Pre { float ds4[4]; };
-    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+    // Piece `pos` (0..3) of super-block sb of a row.
+    static __device__ __forceinline__ Raw load_at(const uint8_t *R, uint32_t o0, uint32_t sb, uint32_t pos) {
         Raw r;
-        const uint32_t hh = (p >> 1) & 1, l0 = 16 * (p & 1);
-        const uint32_t B = o0 + 210 * (p >> 2);
-        load16_u(R, B + 64 * hh + l0, r.ql0);
-        load16_u(R, B + 64 * hh + 32 + l0, r.ql1);
-        load16_u(R, B + 128 + 32 * hh + l0, r.qhx);
+        const uint32_t hh = pos >> 1, l0 = 16 * (pos & 1);
+        // offsets inside the super-block (fixed per lane in the walks), then
+        // its start: sb < 2^24 (k < 2^32), so a full-rate 24-bit multiply
+        const uint32_t oql = 64 * hh + l0, oqh = 128 + 32 * hh + l0, osc = 192 + 8 * hh;
+        const uint32_t B = o0 + __umul24(sb, 210u);
+        load16_u(R, B + oql, r.ql0);
+        load16_u(R, B + (oql + 32), r.ql1);
+        load16_u(R, B + oqh, r.qhx);
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.qhx[i] ^= 0xAAAAAAAAu;  // invert bit 1 of every 2-bit high part
-        const u32x2a2 v = ldv<u32x2a2>(R, B + 192 + 8 * hh);  // sc[8hh .. 8hh+7]
-        r.sc[0] = v.x;
-        r.sc[1] = v.y;
+        const u32x2a2 v = ldv<u32x2a2>(R, B + osc);  // sc[8hh .. 8hh+7]
+        // bytes (pos & 1) + 0, 2, 4, 6 of the eight (v_perm_b32: selector 0-3 = v.x, 4-7 = v.y)
+        r.s4 = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u + 0x01010101u * (pos & 1));
         r.d = ld16(R, B + 208);
         return r;
     }
-    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t p) {
+    static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        return load_at(R, o0, p >> 2, p & 3);
+    }
+    // The mat-vec walks: every piece whose values are used has p % 4 == lane % 4
+    // (a lane's pieces are lane + (a multiple of the lanes per row)), so the
+    // position inside the super-block comes from the lane and its offsets
+    // stay fixed across the walk; other loads (clamped or past the last item)
+    // stay inside the super-block p / 4 and are never used.
+    static __device__ __forceinline__ Raw load_walk(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
+        return load_at(R, o0, p >> 2, threadIdx.x & 3u);
+    }
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) {
         Pre pr;
-        const float d = h2f(r.d);
+        const float d4 = h2f(r.d) * 0.25f;  // exact (a power of two, far from underflow)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t idx = 2 * t + (p & 1);
-            const int8_t s = (int8_t)(r.sc[idx >> 2] >> (8 * (idx & 3)));
-            pr.ds4[t] = d * (float)s * 0.25f;  // exact: d*sc, then a power of two
-        }
+        for (int t = 0; t < 4; ++t) pr.ds4[t] = d4 * (float)(int8_t)(r.s4 >> (8 * t));  // exact: d*sc/4
         return pr;
     }
     // Four values at a time: byte i becomes the int8 4*(q_i - 32) (low 4
@@ -440,6 +452,14 @@ template <> struct Tr<kQ6K> : Geo<kQ6K> {
     static constexpr uint32_t goff(int g) { return 32 * (g >> 2) + 4 * (g & 3); }
     static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
 };
+
+template <int T>
+__device__ __forceinline__ typename Tr<T>::Raw load_walk(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t k) {
+    if constexpr (T == kQ6K)
+        return Tr<T>::load_walk(R, o0, p, k);
+    else
+        return Tr<T>::load(R, o0, p, k);
+}
 
 // Per-row output scale of the fused normalisation (part == NULL: none).
 struct RowScale {
@@ -922,18 +942,18 @@ __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *c
     if (p >= pe) return;
     Raw A[NR], B[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) A[r] = TR::load(R[r], o0[r], p, k);
+    for (int r = 0; r < NR; ++r) A[r] = load_walk<T>(R[r], o0[r], p, k);
     while (true) {
         const uint32_t p1 = p + 64;
         const bool m1 = p1 < pe;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) B[r] = TR::load(R[r], o0[r], m1 ? p1 : p, k);
+        for (int r = 0; r < NR; ++r) B[r] = load_walk<T>(R[r], o0[r], m1 ? p1 : p, k);
         compute_piece<T, M, NR>(acc, A, p, vb, xs, XS, k, sx, SXS);
         if (!m1) break;
         const uint32_t p2 = p1 + 64;
         const bool m2 = p2 < pe;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) A[r] = TR::load(R[r], o0[r], m2 ? p2 : p1, k);
+        for (int r = 0; r < NR; ++r) A[r] = load_walk<T>(R[r], o0[r], m2 ? p2 : p1, k);
         compute_piece<T, M, NR>(acc, B, p1, vb, xs, XS, k, sx, SXS);
         if (!m2) break;
         p = p2;
@@ -970,7 +990,7 @@ __device__ __forceinline__ void load_item(const uint8_t *Wb, const MvArgs &a, ui
     uint32_t o0[NR];
     row_bases<NR>(Wb, a.row_bytes, a.n, (g * NR) << (6 - lpr_of<SUB>(a)), SUB, slot * NR, R, o0);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) raw[r] = Tr<T>::load(R[r], o0[r], p, a.k);
+    for (int r = 0; r < NR; ++r) raw[r] = load_walk<T>(R[r], o0[r], p, a.k);
 }
 
 // The group's outputs, with the tree for the lanes-per-row of this k.
