@@ -1,0 +1,76 @@
+"""bench.py's host logic on the CPU: the HBM traffic record is built from
+rocprofv3 counter files exactly as documented (FETCH_SIZE / WRITE_SIZE in KiB
+per dispatch, each scaled by what the counter reads for a plain copy of known
+size), kernels are matched to m by their template arguments, and a record
+taken on other kernel sources is not reported."""
+import csv
+import json
+import os
+
+import pytest
+
+import bench
+
+HDR = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(folder, name, rows):
+    os.makedirs(folder, exist_ok=True)
+    with open(os.path.join(folder, name), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(HDR)
+        w.writerows(rows)
+
+
+def _kernel(m, nr, unc):
+    return f"void rex::mv_kernel<1, {m}, {nr}, false, false, {str(unc).lower()}>(rex::MvArgs)"
+
+
+@pytest.fixture
+def counters(tmp_path):
+    d = tmp_path
+    # two dispatches per kernel (mean taken), an unrelated kernel that must be ignored
+    _write(d / "f" / "host", "bench_counter_collection.csv", [
+        [1, _kernel(1, 1, False), "FETCH_SIZE", 8800.0], [2, _kernel(1, 1, False), "FETCH_SIZE", 8900.0],
+        [3, _kernel(8, 2, False), "FETCH_SIZE", 9330.0], [4, _kernel(8, 2, False), "FETCH_SIZE", 9330.0],
+        [5, "void stream_read_kernel<4>(...)", "FETCH_SIZE", 1e9]])
+    _write(d / "w", "bench_counter_collection.csv", [
+        [1, _kernel(1, 1, False), "WRITE_SIZE", 16.0], [2, _kernel(1, 1, False), "WRITE_SIZE", 16.0],
+        [3, _kernel(8, 2, False), "WRITE_SIZE", 128.0], [4, _kernel(8, 2, False), "WRITE_SIZE", 128.0]])
+    # calibration: a fill (reads nothing) and copies of 256 MiB; the copy reads half its bytes
+    _write(d / "cf", "copy_counter_collection.csv", [
+        [1, "FillFunctor", "FETCH_SIZE", 16.0], [2, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 131072.0],
+        [3, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 131072.0]])
+    _write(d / "cw", "copy_counter_collection.csv", [
+        [1, "FillFunctor", "WRITE_SIZE", 262144.0], [2, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 262144.0]])
+    return d
+
+
+def test_write_traffic_scales_counters_by_the_copy(counters, monkeypatch, tmp_path):
+    out_root = tmp_path / "root"
+    os.makedirs(out_root / "profiles")
+    monkeypatch.setattr(bench, "ROOT", str(out_root))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "abc")
+    d = counters
+    bench.write_traffic(str(d / "f"), str(d / "w"), str(d / "cf"), str(d / "cw"), bench.copy_calibration_bytes(256))
+    rec = json.load(open(out_root / "profiles" / "traffic.json"))
+    assert rec["kernel_source_hash"] == "abc"
+    assert rec["copy_calibration"]["fetch_factor"] == pytest.approx(0.5)
+    assert rec["copy_calibration"]["write_factor"] == pytest.approx(1.0)
+    l1, l8 = rec["launches"]["q8_0_4096x4096:m1"], rec["launches"]["q8_0_4096x4096:m8"]
+    assert l1["dispatches"] == 2 and l8["dispatches"] == 2
+    assert l1["fetch_bytes"] == round(8850.0 * 1024 / 0.5)          # mean KiB, / fetch factor
+    assert l1["write_bytes"] == 16 * 1024
+    assert l8["hbm_bytes"] == round(9330.0 * 1024 / 0.5) + 128 * 1024
+    # algorithmic bytes: weights + x (m rows of k floats) + y (m rows of n floats)
+    assert l1["algorithmic_bytes"] == 4096 * 4096 // 32 * 34 + 4 * 4096 + 4 * 4096
+    assert l8["algorithmic_bytes"] == 4096 * 4096 // 32 * 34 + 8 * 4 * 4096 + 8 * 4 * 4096
+    # the record is reported only for the sources it was taken on
+    assert bench.measured_traffic("q8_0_4096x4096", 8) == l8["hbm_bytes"]
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "other")
+    assert bench.measured_traffic("q8_0_4096x4096", 8) is None
+
+
+def test_copy_calibration_size_is_whole_vectors():
+    assert bench.copy_calibration_bytes(256) == 256 << 20
+    assert bench.copy_calibration_bytes(0.001) % 16 == 0
