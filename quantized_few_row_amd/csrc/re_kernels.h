@@ -45,8 +45,10 @@
 
 // Code-generation knobs (measured defaults; variants with other values,
 // and with register caps for more waves per SIMD, measured no faster): the
-// smallest m whose piece loop gets a scheduling barrier per group, and the
-// register budget that allows two items of loads in flight.
+// smallest m whose piece loop gets a scheduling barrier per group, the
+// register budget that allows two items of loads in flight, the largest m
+// whose x is requested ahead of the weights, and the smallest m at which
+// half of a workgroup's waves request their weights after the x staging.
 #ifndef REX_SCHED_BARRIER_MIN_M
 #define REX_SCHED_BARRIER_MIN_M 4
 #endif
@@ -55,6 +57,9 @@
 #endif
 #ifndef REX_X_FIRST_MAX_M
 #define REX_X_FIRST_MAX_M 2
+#endif
+#ifndef REX_LATE_HALF_MIN_M
+#define REX_LATE_HALF_MIN_M 5
 #endif
 
 
@@ -1141,10 +1146,19 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             // the weights, so the barrier does not wait for every wave's weights
             stage_x_first<T, M>(xs, xb, a.xrs, a.k, XS, prefetch_first);
         } else {
-            prefetch_first();
+            // From REX_LATE_HALF_MIN_M input rows on, the upper half of the
+            // workgroup's waves request their first items only after the
+            // staging barrier: the lower half's weights then arrive sooner
+            // and their multiply overlaps the later loads (Q8_0 4096 x 4096
+            // at m = 6 / 8: -4.9% / -3.6%, BF16 -2.5% / -1.6%, Q4_K and
+            // Q6_K unchanged; mixed at m = 4).
+            const bool late = M >= REX_LATE_HALF_MIN_M && nwaves >= 2 && wave >= (nwaves >> 1);
+            if (!late) prefetch_first();
             stage_x<T, M>(xs, xb, a.xrs, 0, a.k, XS);
+            __syncthreads();
+            if (late) prefetch_first();
         }
-        __syncthreads();
+        if constexpr (NORM || M <= REX_X_FIRST_MAX_M) __syncthreads();
         if constexpr (kOffsets<T>) {
             stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, a.k);
             __syncthreads();
