@@ -97,7 +97,10 @@ typedef struct {
  *  rows_per_wave        : packing.  Weight rows a wave streams together,
  *                         sharing each input load: 1, 2 or 4.
  *  waves_per_workgroup  : packing.  1..8 (64..512 threads).
- *  workgroups_per_batch : packing.  Grid x; batch is grid y (batch-major).
+ *  workgroups_per_batch : packing.  Workgroups per batch entry; the grid
+ *                         holds workgroups_per_batch x batch of them,
+ *                         flattened batch-fastest (workgroup w of entry b
+ *                         is w * batch + b).
  *  k_chunk              : packing.  Input values per row staged in LDS per
  *                         pass; >= k means one pass.  Otherwise a multiple of
  *                         the weight type's wave step (512 values for F16 /

@@ -494,6 +494,7 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     a.groups_per_batch = (n + rg - 1) / rg;
     uint32_t wgs = sch.workgroups_per_batch < a.groups_per_batch ? sch.workgroups_per_batch : a.groups_per_batch;
     a.groups_per_wg = (a.groups_per_batch + wgs - 1) / wgs;
+    a.batch = batch;
     wgs = (a.groups_per_batch + a.groups_per_wg - 1) / a.groups_per_wg;  // as the kernel recomputes it
     const uint32_t step = wave_step_values(t);
     if (sch.k_chunk >= k) {

@@ -38,6 +38,7 @@ struct MvArgs {
     float eps;
     uint32_t norm_offset;       // byte offset in LDS of the m per-row inverse RMS values (double)
     uint32_t walk_unconditional;  // 1: waves hold more items than the load depth (see fetch_item)
+    uint32_t batch;               // batch entries (grid = workgroups per entry x batch)
     // Types whose weights carry a per-segment offset (Q4_K: - dmin * mn):
     // the sums of the staged input over each 32-value segment, per input
     // row, at byte offset sx_offset in LDS, sx_stride floats per row.

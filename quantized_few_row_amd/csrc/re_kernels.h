@@ -1089,9 +1089,14 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t nwaves = blockDim.x >> 6;
-    const uint32_t wgs_per_batch = (a.groups_per_batch + a.groups_per_wg - 1) / a.groups_per_wg;
-    const uint32_t b = blockIdx.x / wgs_per_batch;  // batch-major flattening
-    const uint32_t w = blockIdx.x - b * wgs_per_batch;
+    // Batch-fastest flattening: workgroup w of batch entry b is w*batch + b.
+    // Workgroups are dispatched round-robin over the 8 XCDs (each with its
+    // own L2), so with a batch that is a multiple of 8 every entry's
+    // workgroups share one XCD and its x is fetched into one L2 instead of
+    // all eight (16 grouped entries at m = 8: -7.6%; batch-1 launches
+    // unaffected).
+    const uint32_t w = blockIdx.x / a.batch;
+    const uint32_t b = blockIdx.x - w * a.batch;
     const float *__restrict__ xb = a.x + b * a.xbs;
     float *__restrict__ yb = a.y + b * a.ybs;
     const uint32_t g0 = w * a.groups_per_wg;
