@@ -1143,9 +1143,16 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             if (DEPTH == 2) fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, B);
         };
         if constexpr (NORM) {
-            prefetch_first();
+            // as below for the plain product: from REX_LATE_HALF_MIN_M input
+            // rows on, the upper half of the waves request their first items
+            // after the normalisation prologue (fused Q8_0 4096 x 4096 at
+            // m = 5..8: -2% to -4%)
+            const bool late = M >= REX_LATE_HALF_MIN_M && nwaves >= 2 && wave >= (nwaves >> 1);
+            if (!late) prefetch_first();
             norm_partials<T, M, true>(part, xs, XS, xb, a.r + b * a.xbs, a.g,
                                       (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);
+            __syncthreads();
+            if (late) prefetch_first();
         } else if constexpr (M <= REX_X_FIRST_MAX_M) {
             // few input rows: x is a few loads per thread, requested ahead of
             // the weights, so the barrier does not wait for every wave's weights
@@ -1163,7 +1170,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             __syncthreads();
             if (late) prefetch_first();
         }
-        if constexpr (NORM || M <= REX_X_FIRST_MAX_M) __syncthreads();
+        if constexpr (!NORM && M <= REX_X_FIRST_MAX_M) __syncthreads();
         if constexpr (kOffsets<T>) {
             stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, a.k);
             __syncthreads();
