@@ -8,8 +8,8 @@
 //     together in the row (F16: 8 values; Q8_0 / Q5_0: one block; Q4_K: 32
 //     nibble bytes, two sub-blocks, of a super-block; Q6_K: a quarter
 //     super-block).  Lane L of the wave owning the row takes pieces L, L+64,
-//     L+128, ... in that order,
-//     so each load instruction of a wave covers adjacent bytes of the row.
+//     L+128, ... in that order, so each load instruction of a wave covers
+//     adjacent bytes of the row.
 //   - A wave streams rows_per_wave (NR) rows at once: every input value read
 //     from LDS feeds NR weight rows ("nr0 rows sharing each input load").
 //   - The m input rows of the batch are staged once per pass into LDS
@@ -310,7 +310,9 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
 // Piece p: super-block p/4, nibble chunk c = p%4 (bytes 32c..32c+31 of its
 // 128): low nibbles are values 64c + 0..31 of sub-block 2c, high nibbles
 // values 64c + 32..63 of sub-block 2c+1.
-// w = fma(d*sc, q, -(dmin*mn)): one rounding of the exact value.
+// The weight value (row_exact_dequant) is w = fma(d*sc, q, -(dmin*mn)): one
+// rounding of the exact value; the mat-vec applies d*sc and dmin*mn per
+// sub-block instead (see SEG).
 template <> struct Tr<kQ4K> : Geo<kQ4K> {
     // One scale and one offset per 32 values (groups 8e..8e+7, sub-block
     // 2c+e): the segment contributes d*sc * sum(q*x) - dmin*mn * sum(x).
