@@ -411,15 +411,57 @@ def cpu_baseline(w, W, x, ms, seconds):
     rows = int(max(1, min(n, seconds / max(per_row, 1e-9))))
     reps = max(1, int(seconds / max(per_row * rows, 1e-9)))  # whole steps, repeated up to ~seconds
     t0 = time.perf_counter()
+    single = {}
     for _ in range(reps):
         for m in ms:
-            oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, rows))
+            single[m] = oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, rows))[0]
     el = time.perf_counter() - t0
     wbytes = rb * rows * batch * len(ms) * reps
-    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{w.name}: first {rows} of {n} output rows x {batch} batch(es) at m={list(ms)}, "
-                      f"{reps} pass(es), float64 dequantize-then-dot, single thread, {el:.1f} s",
-            "seconds": round(el, 2)}
+    out = {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{w.name}: first {rows} of {n} output rows x {batch} batch(es) at m={list(ms)}, "
+                     f"{reps} pass(es), float64 dequantize-then-dot, single thread, {el:.1f} s",
+           "seconds": round(el, 2)}
+    out["parallel"] = cpu_baseline_parallel(w, W, x, ms, rows, reps, single)
+    return out
+
+
+def cpu_baseline_parallel(w, W, x, ms, rows, reps, single):
+    """The same oracle sample split over host threads by output rows (each
+    thread calls the unchanged oracle on its row range; the calls run
+    outside the interpreter lock), checked identical to the single-thread
+    results."""
+    import threading
+
+    import numpy as np
+
+    import oracle
+    t, n, k, batch = w.wtype, w.n, w.k, w.batch
+    xrs, xbs, _, _ = w.strides(8)
+    threads = max(1, min(16, os.cpu_count() or 1, rows))  # the host share of one GPU
+    bounds = [(rows * i // threads, rows * (i + 1) // threads) for i in range(threads)]
+    got = {m: [None] * threads for m in ms}
+
+    def work(i):
+        lo, hi = bounds[i]
+        for _ in range(reps):
+            for m in ms:
+                got[m][i] = oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(lo, hi))[0]
+
+    pool = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    t0 = time.perf_counter()
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join()
+    el = time.perf_counter() - t0
+    same = True
+    for m in ms:
+        for i, (lo, hi) in enumerate(bounds):
+            same &= bool(np.array_equal(got[m][i][..., lo:hi], single[m][..., lo:hi]))
+    wbytes = oracle.row_bytes(t, k) * rows * batch * len(ms) * reps
+    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the same sample split by output rows over {threads} host threads, {el:.1f} s",
+            "identical_to_single_thread": same, "seconds": round(el, 2)}
 
 
 def sweep(path, steps):
