@@ -56,7 +56,7 @@
 #define REX_DEPTH_BUDGET 120
 #endif
 #ifndef REX_X_FIRST_MAX_M
-#define REX_X_FIRST_MAX_M 2
+#define REX_X_FIRST_MAX_M 4
 #endif
 #ifndef REX_LATE_HALF_MIN_M
 #define REX_LATE_HALF_MIN_M 5
@@ -634,12 +634,12 @@ template <int T, int M, typename F>
 __device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
                                               uint32_t k, uint32_t XS, F &&between) {
     // Chunks per thread requested ahead of the weights: at 512 threads, all
-    // of x up to k = 4096 (m = 1) or 8192 (m = 2).  The rest goes behind the
-    // weights, and the staging barrier then waits for them too.  At m = 2 a
-    // whole k = 4096 row ahead measured 2-11% faster than half of it; at
-    // m = 1 more chunks ahead cost occupancy (the staging registers exceed
-    // the walk's) and measured 15-75% slower.
-    constexpr int U = M >= 2 ? 4 : 2;
+    // of x up to k = 4096 (m = 1, m >= 5) or 8192 (m = 2..4).  The rest goes
+    // behind the weights, and the staging barrier then waits for them too.
+    // At m = 2..4 a whole k = 4096 row ahead measured 2-12% faster than half
+    // of it; at m = 1 more chunks ahead cost occupancy (the staging
+    // registers exceed the walk's) and measured 15-75% slower.
+    constexpr int U = (M >= 2 && M <= 4) ? 4 : 2;
     const uint32_t n4 = k >> 2;
     const uint32_t nt = blockDim.x;
     f32x4 v[U][M];
