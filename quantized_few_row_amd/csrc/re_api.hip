@@ -329,14 +329,18 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     const uint64_t wave_rows = rows >> (6 - lpr);
     uint32_t nr = max_rows_per_wave(t, m);
     while (nr > 1 && wave_rows / nr < target_waves) nr >>= 1;
-    // Up to 4 input rows and fewer than 16 rows per wave: single rows, so
-    // each wave walks more items with loads in flight behind the multiply
-    // (measured 3-18% faster than 2 or 4 rows per wave at m = 2..4 on
-    // 4096 x 4096 Q8_0, BF16, F32, 14336 x 4096 Q4_K and 16 x 1024 x 4096
-    // Q5_0; the 128256-row head keeps 4).  Short rows (a wave already
-    // covers 2 or 4 rows per item) and the fused-norm instances measured
-    // slower with it and keep the rule above.
-    if (m <= 4 && kc >= k && lpr == 6 && !fused_norm && wave_rows < 16 * target_waves) nr = 1;
+    // Up to 4 input rows and fewer than 16 rows per wave: single rows for
+    // rows of several wave steps, so each wave walks more items with loads
+    // in flight behind the multiply (3-10% faster than 2 or 4 rows per wave
+    // at m = 3..4 on 4096 x 4096 Q8_0, BF16, F32 and 16 x 1024 x 4096 Q5_0);
+    // rows of one wave step take 2 (each x value then feeds two rows;
+    // 14336 x 4096 Q4_K at m = 4: -7% against single rows).  The
+    // 128256-row head keeps 4.  Short rows (a wave already covers 2 or 4
+    // rows per item) and the fused-norm instances measured slower with it
+    // and keep the rule above.
+    const uint32_t steps = (pieces_of(t, k) + 63) >> 6;
+    if (m <= 4 && kc >= k && lpr == 6 && !fused_norm && wave_rows < 16 * target_waves)
+        nr = steps >= 2 ? 1u : (nr < 2u ? nr : 2u);  // never more than leaves 8 waves per CU
     s.rows_per_wave = nr;
     const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
     const uint32_t gpb = (n + rg - 1) / rg;
