@@ -325,6 +325,13 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         s.waves_per_workgroup = waves;
         const uint32_t max_wgs = (gpb + waves - 1) / waves;
         uint64_t w = (target / waves + batch - 1) / batch;
+        // as for more input rows below: no more workgroups than keep each
+        // one's weight bytes at or above the m*k*4 bytes of x it stages
+        // (Q6_K 4096 x 14336 at m = 2: 512 -> 256 workgroups, -16%)
+        const uint64_t x_wg = (uint64_t)m * k * sizeof(float);
+        const u128 by_x = (u128)rows * row_bytes_of(t, k) / x_wg / di.cus * di.cus;
+        const uint64_t cap = by_x > di.cus ? (uint64_t)by_x : (uint64_t)di.cus;
+        if (w > (cap + batch - 1) / batch) w = (cap + batch - 1) / batch;
         if (w < 1) w = 1;
         s.workgroups_per_batch = (uint32_t)(w < max_wgs ? w : max_wgs);
         return 0;
