@@ -47,8 +47,9 @@
 // and with register caps for more waves per SIMD, measured no faster): the
 // smallest m whose piece loop gets a scheduling barrier per group, the
 // register budget that allows two items of loads in flight, the largest m
-// whose x is requested ahead of the weights, and the smallest m at which
-// half of a workgroup's waves request their weights after the x staging.
+// whose x is requested ahead of the weights, the smallest m at which half
+// of a workgroup's waves request their weights after the x staging, and the
+// smallest m from which waves of three or more items take x ahead instead.
 #ifndef REX_SCHED_BARRIER_MIN_M
 #define REX_SCHED_BARRIER_MIN_M 4
 #endif
@@ -60,6 +61,9 @@
 #endif
 #ifndef REX_LATE_HALF_MIN_M
 #define REX_LATE_HALF_MIN_M 5
+#endif
+#ifndef REX_X_FIRST_UNC_MIN_M
+#define REX_X_FIRST_UNC_MIN_M 6
 #endif
 
 
@@ -1145,7 +1149,15 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         // the unconditional walk and for x staged ahead of them (so that the
         // x loads can be waited for without them); under a branch otherwise
         // (measured faster for waves of one or two items at m >= 3).
-        constexpr bool UP = UNC || M <= REX_X_FIRST_MAX_M;
+        // x ahead of the weights: up to REX_X_FIRST_MAX_M input rows, and
+        // from REX_X_FIRST_UNC_MIN_M on in the unconditional walk (three or
+        // more items per wave: the walk staggers the later items' loads
+        // itself, and the barrier should not wait behind the first ones;
+        // m = 6 / 8: BF16 -3%, Q4_K -1% / -5%, F32 -1% / -2%; at m = 5 it
+        // measured mixed, up to +4%); waves of one or two items take the
+        // late half-workgroup issue below instead.
+        constexpr bool XF = M <= REX_X_FIRST_MAX_M || (UNC && M >= REX_X_FIRST_UNC_MIN_M);
+        constexpr bool UP = UNC || XF;
         auto prefetch_first = [&] {
             fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, A);
             if (DEPTH == 2) fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, B);
@@ -1161,9 +1173,9 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                                       (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);
             __syncthreads();
             if (late) prefetch_first();
-        } else if constexpr (M <= REX_X_FIRST_MAX_M) {
-            // few input rows: x is a few loads per thread, requested ahead of
-            // the weights, so the barrier does not wait for every wave's weights
+        } else if constexpr (XF) {
+            // x is a few loads per thread, requested ahead of the weights, so
+            // the barrier does not wait for every wave's weights
             stage_x_first<T, M>(xs, xb, a.xrs, a.k, XS, prefetch_first);
         } else {
             // From REX_LATE_HALF_MIN_M input rows on, the upper half of the
@@ -1178,7 +1190,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             __syncthreads();
             if (late) prefetch_first();
         }
-        if constexpr (!NORM && M <= REX_X_FIRST_MAX_M) __syncthreads();
+        if constexpr (!NORM && XF) __syncthreads();
         if constexpr (kOffsets<T>) {
             stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, a.k);
             __syncthreads();
