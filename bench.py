@@ -11,15 +11,16 @@ time between two stream synchronisations around the replay.
 Prints one JSON line.  ``value`` is effective weight GB/s over the whole job
 (weight bytes of every call / wall time).  ``roofline`` is for the step's
 dominant (longest) kernel, whose mean duration comes from HIP events around
-back-to-back launches on the bench stream.  Its bound follows from its
-arithmetic intensity: below the ridge of the HBM roof (8 TB/s) and the FP32
-vector-ALU roof (256 CUs x 64 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s; the
-kernels use no packed FP32) it is "hbm" and ``achieved`` is algorithmic bytes
-(weights + x + y) per second; above it, "alu" and algorithmic flops (2nmk per
-batch) per second.  ``attainable_read`` is the fastest plain read of the same
-weight bytes (include/row_exact_probe.h), the practical ceiling for the
-weight stream at this size.  ``cpu_baseline`` times the oracle (float64 CPU
-reference) on a bounded sample of the same workload.
+back-to-back launches on the bench stream: the HBM roof (8 TB/s) with
+``achieved`` = algorithmic bytes (weights + x + y) per second, and, as a
+secondary figure, the kernel's algorithmic flops (2nmk per batch entry) per
+second against the published FP32 vector peak (157.3 TFLOP/s; the kernels
+issue unpacked FMAs, whose roof is half of it).  ``attainable_read`` is the
+fastest plain read of the same weight bytes (include/row_exact_probe.h), the
+practical ceiling for the weight stream at this size.  ``host_us_per_call``
+is the host time of one eager C-ABI call.  ``cpu_baseline`` times the oracle
+(float64 CPU reference) on a bounded sample of the same workload, split by
+output rows over the host threads one GPU's share of the machine allows.
 """
 from __future__ import annotations
 
@@ -34,10 +35,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
-# FP32 FMA issue rate of the vector ALUs: 256 CUs x 64 lanes x 2 flops x 2.4 GHz.
-# (Packed FP32, which doubles it to the published 157.3 TFLOP/s, is not used:
-# the kernels are built with packed-FP32 selection off.)
+# Published FP32 vector peak of MI355X (packed FP32: two FMAs per lane per clock).
+FP32_PUBLISHED_TFLOPS = 157.3
+# FP32 FMA issue rate of the vector ALUs without packed FP32, which these
+# kernels do not use: 256 CUs x 64 lanes x 2 flops x 2.4 GHz.
 VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+# Host threads one GPU's share of the box may use (16 CPUs per GPU).
+HOST_THREADS_PER_GPU = 16
 METRIC = "effective weight GB/s and % of HBM peak, quantized GEMV at m=1/4/8"
 
 
@@ -52,6 +56,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--sweep", default="", help="write per-(workload, m) kernel timings to this JSON file")
+    ap.add_argument("--schedule-sweep", default="",
+                    help="time the default schedule against pinned packings for the workloads named with "
+                         "--sweep-workloads (default: the held-out shapes) and write the results to this JSON file")
+    ap.add_argument("--sweep-workloads", default="", help="comma-separated workload names for --schedule-sweep")
     ap.add_argument("--profile-only", action="store_true",
                     help="launch the timed steps eagerly and exit (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -77,17 +85,18 @@ def kernel_source_hash():
 
 def measured_traffic(workload, m):
     """HBM bytes per launch of the (workload, m) kernel from the committed
-    rocprofv3 --pmc summary, or None when it is missing or stale."""
+    rocprofv3 --pmc summary, or None when it is missing or was taken on other
+    kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
     ent = rec.get("launches", {}).get(f"{workload}:m{m}")
-    return None if ent is None else ent.get("hbm_bytes")
+    if ent is None or ent.get("kernel_source_hash", rec.get("kernel_source_hash")) != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes")
 
 
 def _counter_rows(folder, counter):
@@ -147,12 +156,24 @@ def write_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes,
             "hbm_bytes": int(round(fb + wb)), "fetch_bytes": int(round(fb)), "write_bytes": int(round(wb)),
             "fetch_size_kib": fk, "write_size_kib": wk, "dispatches": len(per[(m, "FETCH_SIZE")]),
             "algorithmic_bytes": w.weight_bytes + xb + yb}
-    rec = {"kernel_source_hash": kernel_source_hash(),
-           "copy_calibration": {"bytes": cal_bytes, "fetch_factor": fetch_factor, "write_factor": write_factor},
-           "launches": launches}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec.pop("kernel_source_hash", None)
+    rec["copy_calibration"] = {"bytes": cal_bytes, "fetch_factor": fetch_factor, "write_factor": write_factor}
+    h = kernel_source_hash()
+    old = rec.get("launches", {})
+    rec["launches"] = {key: e for key, e in old.items() if not key.startswith(workload + ":")}
+    for key, e in launches.items():
+        e["kernel_source_hash"] = h
+        rec["launches"][key] = e
+    rec["launches"] = dict(sorted(rec["launches"].items()))
+    with open(path, "w") as f:
         json.dump(rec, f, indent=1)
-    print(json.dumps(rec, indent=1))
+    print(json.dumps({"copy_calibration": rec["copy_calibration"], "launches": launches}, indent=1))
 
 
 def main():
@@ -160,7 +181,11 @@ def main():
     if args.write_traffic:
         if not args.copy_calibration:
             raise SystemExit("bench.py: --write-traffic needs --copy-calibration MIB (the size of the calibration copy)")
-        write_traffic(*args.write_traffic, copy_calibration_bytes(args.copy_calibration))
+        write_traffic(*args.write_traffic, copy_calibration_bytes(args.copy_calibration), workload=args.workload)
+        return
+    if args.schedule_sweep:
+        names = [v for v in args.sweep_workloads.split(",") if v] or None
+        schedule_sweep(args.schedule_sweep, names)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the mat-vec shards by weight rows with no "
@@ -295,6 +320,26 @@ def main():
         read_us.append(e0.elapsed_time(e1) * 1e3 / reps)
     attainable = rbytes / (min(read_us) * 1e-6) / 1e9
 
+    # Host time of one eager call: the C-ABI call (validation, schedule, launch)
+    # timed from Python in a loop of ctypes calls, next to the same loop over
+    # an entry point that does nothing (ctypes' own cost).  The launches queue
+    # behind a spin kernel, so the GPU never back-pressures the host.
+    host_us = {}
+    reps_h = 200
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2e8))
+        t0 = time.perf_counter()
+        for r in range(reps_h):
+            lib.row_exact_launch_count()
+        floor = (time.perf_counter() - t0) / reps_h * 1e6
+        for m in ms:
+            t0 = time.perf_counter()
+            for r in range(reps_h):
+                launch(i + r, m)
+            host_us[f"m{m}"] = round((time.perf_counter() - t0) / reps_h * 1e6, 3)
+    torch.cuda.synchronize()
+    host_us["ctypes_floor"] = round(floor, 3)
+
     # Whole-job timing: graph replay of the same K steps (or eager with --eager).
     y_eager = {m: ybufs[m].clone() for m in ms}
     if args.eager:
@@ -326,13 +371,8 @@ def main():
     _, xb_dom, yb_dom = qfr.row_exact_required_bytes(t, n, k, dom, batch, strides)
     alg_bytes = wbytes + xb_dom + yb_dom
     flops = {mm: 2.0 * n * k * mm * batch for mm in ms}
-    ridge = VALU_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flops per byte where the two roofs meet
-    if flops[dom] / alg_bytes > ridge:
-        bound, unit, peak = "alu", "TFLOP/s", round(VALU_PEAK_TFLOPS, 1)
-        achieved = flops[dom] / (kernel_us[dom] * 1e-6) / 1e12
-    else:
-        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
-        achieved = alg_bytes / (kernel_us[dom] * 1e-6) / 1e9
+    achieved = alg_bytes / (kernel_us[dom] * 1e-6) / 1e9
+    tflops = flops[dom] / (kernel_us[dom] * 1e-6) / 1e12
 
     out = {
         "metric": METRIC,
@@ -359,20 +399,23 @@ def main():
                            "weight_GBps": round(wbytes / (kernel_us[m] * 1e-6) / 1e9, 1),
                            "hbm_frac": round(wbytes / (kernel_us[m] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "frac_of_attainable_read": round(min(read_us) / kernel_us[m], 4),
-                           "valu_TFLOPs": round(flops[m] / (kernel_us[m] * 1e-6) / 1e12, 2),
-                           "valu_frac": round(flops[m] / (kernel_us[m] * 1e-6) / 1e12 / VALU_PEAK_TFLOPS, 4)}
+                           "fp32_TFLOPs": round(flops[m] / (kernel_us[m] * 1e-6) / 1e12, 2),
+                           "fp32_frac_of_published": round(flops[m] / (kernel_us[m] * 1e-6) / 1e12
+                                                           / FP32_PUBLISHED_TFLOPS, 4)}
                   for m in ms},
+        "host_us_per_call": host_us,
         "kernel_source_hash": kernel_source_hash(),
         "roofline": {
             "kernel": f"mv_kernel<{wl.TYPE_NAMES[t]}, m={dom}>",
-            "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.workload, dom),
-            "peak_basis": ("unpacked FP32 FMA: 256 CUs x 64 lanes x 2 flops x 2.4 GHz (packed FP32 is "
-                           "disabled in this build; the published 157.3 TFLOP/s counts two FMAs per lane)"
-                           if bound == "alu" else "MI355X HBM3E, 8 TB/s"),
-            "frac_of_published_fp32": (round(achieved / 157.3, 4) if bound == "alu" else None),
-            "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops[dom],
-            "mean_launch_us": round(kernel_us[dom], 3),
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, dom),
+            "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_us": round(kernel_us[dom], 3),
+            "alu": {"achieved": round(tflops, 2), "peak": FP32_PUBLISHED_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / FP32_PUBLISHED_TFLOPS, 4),
+                    "frac_of_unpacked_fma_peak": round(tflops / VALU_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": flops[dom],
+                    "note": "published FP32 peak counts packed FMAs (two per lane per clock); these kernels "
+                            "issue unpacked FMAs, whose roof is 78.6 TFLOP/s"},
         },
     }
     if not args.no_cpu_baseline:
@@ -383,16 +426,46 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def host_threads():
+    """Threads for the CPU baseline: the CPUs this process may run on, at most
+    one GPU's share of the box."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return max(1, min(avail, HOST_THREADS_PER_GPU)), avail
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, W, x, ms, seconds):
-    """The oracle, single-threaded, on whole rows of the same workload: the
-    first S output rows at every m of the step, S chosen from a short probe so
-    the sample takes about ``seconds``."""
+    """The oracle on whole output rows of the same workload, split by output
+    rows over the host threads (each thread calls the unchanged oracle on its
+    row range; the calls run outside the interpreter lock): the first S rows
+    at every m of the step, S chosen from a short single-thread probe so the
+    multi-thread sample takes about ``seconds``.  The same sample is then run
+    on one thread, and both results are checked identical."""
+    import threading
+
+    import numpy as np
+
     import oracle
     t, n, k, batch = w.wtype, w.n, w.k, w.batch
     xrs, xbs, _, _ = w.strides(8)
     rb = oracle.row_bytes(t, k)
-    probe = max(1, min(n, 16))
-    if w.experts:  # gathered product: whole calls
+    threads, avail = host_threads()
+    host = {"nproc": os.cpu_count(), "cpus_available": avail, "cpu_model": cpu_model()}
+    if w.experts:  # gathered product: whole calls, one thread
         ids = w.make_ids()
         t0 = time.perf_counter()
         reps = 0
@@ -403,41 +476,16 @@ def cpu_baseline(w, W, x, ms, seconds):
         el = time.perf_counter() - t0
         return {"value": round(rb * n * batch * len(ms) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
                 "kind": "oracle", "sample": f"{w.name}: {reps} whole step(s) at m={list(ms)}, float64 "
-                                            f"dequantize-then-dot, single thread, {el:.1f} s", "seconds": round(el, 2)}
+                                            f"dequantize-then-dot, single thread, {el:.1f} s",
+                "seconds": round(el, 2), **host}
+    probe = max(1, min(n, 16))
     t0 = time.perf_counter()
     for m in ms:
         oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, probe))
     per_row = (time.perf_counter() - t0) / probe
-    rows = int(max(1, min(n, seconds / max(per_row, 1e-9))))
-    reps = max(1, int(seconds / max(per_row * rows, 1e-9)))  # whole steps, repeated up to ~seconds
-    t0 = time.perf_counter()
-    single = {}
-    for _ in range(reps):
-        for m in ms:
-            single[m] = oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, rows))[0]
-    el = time.perf_counter() - t0
-    wbytes = rb * rows * batch * len(ms) * reps
-    out = {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"{w.name}: first {rows} of {n} output rows x {batch} batch(es) at m={list(ms)}, "
-                     f"{reps} pass(es), float64 dequantize-then-dot, single thread, {el:.1f} s",
-           "seconds": round(el, 2)}
-    out["parallel"] = cpu_baseline_parallel(w, W, x, ms, rows, reps, single)
-    return out
-
-
-def cpu_baseline_parallel(w, W, x, ms, rows, reps, single):
-    """The same oracle sample split over host threads by output rows (each
-    thread calls the unchanged oracle on its row range; the calls run
-    outside the interpreter lock), checked identical to the single-thread
-    results."""
-    import threading
-
-    import numpy as np
-
-    import oracle
-    t, n, k, batch = w.wtype, w.n, w.k, w.batch
-    xrs, xbs, _, _ = w.strides(8)
-    threads = max(1, min(16, os.cpu_count() or 1, rows))  # the host share of one GPU
+    # rows for about `seconds` on all threads (assuming a near-linear speed-up)
+    rows = int(max(threads, min(n, seconds * threads / max(per_row, 1e-9))))
+    reps = max(1, int(seconds * threads / max(per_row * rows, 1e-9)))
     bounds = [(rows * i // threads, rows * (i + 1) // threads) for i in range(threads)]
     got = {m: [None] * threads for m in ms}
 
@@ -454,14 +502,24 @@ def cpu_baseline_parallel(w, W, x, ms, rows, reps, single):
     for th in pool:
         th.join()
     el = time.perf_counter() - t0
+    wbytes = rb * rows * batch * len(ms) * reps
+    out = {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{w.name}: first {rows} of {n} output rows x {batch} batch(es) at m={list(ms)}, "
+                     f"{reps} pass(es), float64 dequantize-then-dot, split by output rows over {threads} "
+                     f"host threads, {el:.1f} s",
+           "seconds": round(el, 2), **host}
+    # the same sample on one thread (one pass), checked identical
+    t0 = time.perf_counter()
     same = True
     for m in ms:
+        y1 = oracle.matvec(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows=(0, rows))[0]
         for i, (lo, hi) in enumerate(bounds):
-            same &= bool(np.array_equal(got[m][i][..., lo:hi], single[m][..., lo:hi]))
-    wbytes = oracle.row_bytes(t, k) * rows * batch * len(ms) * reps
-    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the same sample split by output rows over {threads} host threads, {el:.1f} s",
-            "identical_to_single_thread": same, "seconds": round(el, 2)}
+            same &= bool(np.array_equal(got[m][i][..., lo:hi], y1[..., lo:hi]))
+    el1 = time.perf_counter() - t0
+    out["single_thread"] = {"value": round(rb * rows * batch * len(ms) / el1 / 1e9, 4), "unit": "GB/s",
+                            "cores": 1, "seconds": round(el1, 2),
+                            "identical_to_multi_thread": same}
+    return out
 
 
 def sweep(path, steps):
@@ -529,9 +587,109 @@ def sweep(path, steps):
                         "hbm_frac": round(w.weight_bytes / us / 1e3 / HBM_PEAK_GBS, 4),
                         "attainable_read_us": round(min(read_us), 3),
                         "frac_of_attainable_read": round(min(read_us) / us, 4),
-                        "valu_frac": round(fl / (us * 1e-6) / 1e12 / VALU_PEAK_TFLOPS, 4),
+                        "fp32_frac_of_published": round(fl / (us * 1e-6) / 1e12 / FP32_PUBLISHED_TFLOPS, 4),
                         "schedule": sch.asdict()})
             print(json.dumps(res[-1]), file=sys.stderr, flush=True)
+        del Wd
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
+def schedule_sweep(path, names=None):
+    """The chooser against pinned packings.  For every m of each workload:
+    the default schedule and pinned ones (rows per wave 1/2/4, 2/4/8 waves per
+    workgroup, 1..32 workgroups per CU or one row group per wave, one or two
+    LDS passes), each timed as the mean of back-to-back launches on cold
+    weights (checked bitwise equal to the default: packing is inert); then
+    the default and the three fastest pinned schedules again, in five
+    interleaved rounds, median per schedule."""
+    import ctypes
+    import itertools
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import quantized_few_row_amd as qfr
+    import workloads as wl
+    names = names or list(wl.HELD_OUT)
+    lib = qfr.load_library()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.Stream()
+    hs = stream.cuda_stream
+    step = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048, wl.F32: 256, wl.BF16: 512}
+    res = []
+    for name in names:
+        w = wl.get(name)
+        t, n, k, batch = w.wtype, w.n, w.k, w.batch
+        xrs, xbs, yrs, ybs = w.strides(8)
+        st = qfr.Strides(xrs, xbs, yrs, ybs)
+        W = w.make_weights()
+        copies = max(2, int(np.ceil((1 << 30) / w.stored_weight_bytes)))
+        Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
+        wp = [Wd[c].data_ptr() for c in range(copies)]
+        xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        for m in w.ms:
+            _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, st)
+            y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
+            d = qfr.row_exact_schedule(t, n, k, m, batch)
+            cands = {}
+            for nr, wv, f in itertools.product((1, 2, 4), (2, 4, 8), (1, 2, 4, 8, 16, 32, 0)):
+                for kc in (k, k // 2):
+                    if kc < k and kc % step[t]:
+                        continue
+                    wgs = max(1, cus * f // wv // batch) if f else 1 << 30
+                    s = qfr.Schedule(d.k_split, nr, wv, wgs, kc)
+                    cands[(nr, wv, f, kc)] = s
+
+            def run(s, i):
+                if s is None:
+                    return lib.row_exact_mv(t, wp[i % copies], xd.data_ptr(), y.data_ptr(), n, k, m, batch,
+                                            ctypes.byref(st), hs)
+                return lib.row_exact_mv_scheduled(t, wp[i % copies], xd.data_ptr(), y.data_ptr(), n, k, m, batch,
+                                                  ctypes.byref(st), ctypes.byref(s), hs)
+
+            def mean_us(s, reps=100):
+                with torch.cuda.stream(stream):
+                    for i in range(3):
+                        run(s, i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda._sleep(int(2e6))
+                    e0.record(stream)
+                    for i in range(reps):
+                        run(s, i)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / reps
+
+            with torch.cuda.stream(stream):
+                run(None, 0)
+            torch.cuda.synchronize()
+            ref = y.clone()
+            timed = {}
+            for key, s in cands.items():
+                with torch.cuda.stream(stream):
+                    rc = run(s, 0)
+                if rc:  # over the device's limits (refused before launch)
+                    continue
+                torch.cuda.synchronize()
+                if not torch.equal(ref.view(torch.int32), y.view(torch.int32)):
+                    raise SystemExit(f"bench.py: schedule {s} changed the bits of {name} m={m}")
+                timed[key] = mean_us(s)
+            best = sorted(timed, key=timed.get)[:3]
+            rounds = {None: [], **{b: [] for b in best}}
+            for _ in range(5):
+                for key in rounds:
+                    rounds[key].append(mean_us(cands[key] if key else None))
+            med = {key: statistics.median(v) for key, v in rounds.items()}
+            best_key = min(best, key=med.get)
+            rec = {"workload": name, "m": m, "default": d.asdict(), "default_us": round(med[None], 3),
+                   "best_pinned": cands[best_key].asdict(), "best_pinned_us": round(med[best_key], 3),
+                   "default_over_best": round(med[None] / med[best_key], 4),
+                   "candidates_timed": len(timed)}
+            res.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
         del Wd
         torch.cuda.empty_cache()
     with open(path, "w") as f:

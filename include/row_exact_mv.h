@@ -46,22 +46,22 @@ extern "C" {
 /* Weight storage (RowExactWeight; same order as its index()).
  *  F16  : row-major [batch*n, k] IEEE half; k % 4 == 0; W 8-byte aligned.
  *  Q8_0 : row-major [batch*n, k/32] blocks of 34 bytes (f16 d, 32 int8);
- *         k % 32 == 0; W 4-byte aligned.
+ *         k % 32 == 0; W 2-byte aligned.
  *  Q4_K : row-major [batch*n, k/256] super-blocks of 144 bytes (f16 d, f16
  *         dmin, 12 bytes of 6-bit scales/mins, 128 bytes of nibbles);
  *         k % 256 == 0; W 16-byte aligned.
  *  Q6_K : row-major [batch*n, k/256] super-blocks of 210 bytes (128 bytes of
  *         low nibbles, 64 bytes of 2-bit highs, 16 int8 scales, f16 d);
- *         k % 256 == 0; W 4-byte aligned.
+ *         k % 256 == 0; W 2-byte aligned.
  *  Q5_0 : row-major [batch*n, k/32] blocks of 22 bytes (f16 d, 32 high bits,
- *         16 bytes of nibbles); k % 32 == 0; W 4-byte aligned.
+ *         16 bytes of nibbles); k % 32 == 0; W 2-byte aligned.
  *  F32  : row-major [batch*n, k] IEEE single; k % 4 == 0; W 16-byte aligned.
  *  BF16 : row-major [batch*n, k] bfloat16 (the upper 16 bits of an IEEE
  *         single); k % 4 == 0; W 8-byte aligned.
  * Block layouts are those of the GGML types of the same names (the pages give
- * their byte sizes only).  The page's dispatcher accepts 2-byte-aligned
- * Q8_0 / Q6_K / Q5_0 weights; this library reads them with dword loads and
- * asks for 4-byte alignment of W (rows inside may sit at any even offset). */
+ * their byte sizes only).  Alignments are the page's validate() weight
+ * alignments for its five types (8 / 2 / 16 / 2 / 2 bytes); no load reads a
+ * byte before W or past its last row. */
 typedef enum {
     ROW_EXACT_F16 = 0,
     ROW_EXACT_Q8_0 = 1,
@@ -121,7 +121,7 @@ typedef struct {
 #define ROW_EXACT_EALIGN (-2)    /* W / x / y pointer alignment */
 #define ROW_EXACT_ESTRIDE (-3)   /* x strides not multiples of 4 */
 #define ROW_EXACT_EALIAS (-4)    /* output views overlap each other, W or x */
-#define ROW_EXACT_EEXTENT (-5)   /* sizes overflow 64-bit byte offsets */
+#define ROW_EXACT_EEXTENT (-5)   /* n >= 2^31, a row over 2^31 - 1 bytes, or sizes past 2^62 bytes */
 #define ROW_EXACT_ESCHEDULE (-6) /* pinned schedule invalid, or over the device's limits */
 #define ROW_EXACT_EHIP (-7)      /* HIP runtime error (device query or launch) */
 
@@ -134,12 +134,14 @@ typedef struct {
  *            j*x_row_stride + kk.
  *  y       : device float32, element (b, j, i) at b*y_batch_stride +
  *            j*y_row_stride + i.  Only these m*n*batch elements are written.
- *  n, k, m, batch : n, k, batch >= 1; 1 <= m <= 8.
+ *  n, k, m, batch : n, k, batch >= 1 (n < 2^31); 1 <= m <= 8.
  *  strides : NULL for contiguous; see row_exact_strides_t.
  *  stream  : HIP stream to enqueue on.
- * Errors: ROW_EXACT_EARG, EALIGN, ESTRIDE, EALIAS (output rows/batches must
- * write disjoint elements, the four layout cases of validate(); y's byte range
- * must not overlap W's or x's), EEXTENT, EHIP. */
+ * Errors: ROW_EXACT_EARG, EALIGN, ESTRIDE, EALIAS (the y layout must nest:
+ * of the row and batch axes with more than one entry, the one with the larger
+ * stride steps past the whole extent of the other, which steps past n values
+ * -- the output-aliasing contract of validate(); y's bytes must not overlap
+ * W's or x's), EEXTENT, EHIP. */
 int row_exact_mv(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n, uint32_t k,
                  uint32_t m, uint32_t batch, const row_exact_strides_t *strides, hipStream_t stream);
 
@@ -203,7 +205,11 @@ int row_exact_mv_add_rmsnorm(row_exact_weight_t wt, const void *W, const float *
 
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
  * depends on (wt, k) only; the packing fields may depend on every argument
- * and on the current device.  Writes *out; errors: EARG, EHIP. */
+ * and on the current device.  Unlike the page's query (weight, rows, k), this
+ * one takes m: the packing is chosen per m because the m-row kernel's
+ * register and LDS needs decide how many rows a wave and how many workgroups
+ * a CU can hold.  m never reaches k_split, so outputs stay row-exact.
+ * Writes *out; errors: EARG, EHIP. */
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                        row_exact_schedule_t *out);
 
@@ -224,14 +230,20 @@ int row_exact_required_bytes(row_exact_weight_t wt, uint32_t n, uint32_t k, uint
                              uint64_t *y_bytes);
 
 /* Enqueue out[r*k + v] = float32 value of weight v of row r, for rows
- * consecutive weight rows at W.  Uses the same device block decoders as the
- * mat-vec.  out must be 4-byte aligned and not overlap W.
+ * consecutive weight rows at W: the weights the product multiplies
+ * (RowExactWeight's storage formats with the block sizes of the page's block
+ * constants, decoded exactly; Q4_K's d*sc*q - dmin*mn rounded once).  Uses
+ * the same device block loads and decoders as the mat-vec, so the values can
+ * be compared bit for bit with an independent decode.  W aligned as for
+ * row_exact_mv; out 4-byte aligned and not overlapping W.
  * Errors: EARG, EALIGN, EALIAS, EEXTENT, EHIP. */
 int row_exact_dequant(row_exact_weight_t wt, const void *W, float *out, uint32_t rows, uint32_t k,
                       hipStream_t stream);
 
-/* Text of the calling thread's last error ("" if none); prefixed
- * "row_exact_mv: ".  Valid until the thread's next call. */
+/* Text of the calling thread's last error ("" if none), the counterpart of
+ * the page's invalid() error (an InvalidArgument message with the op's name
+ * as prefix): prefixed "row_exact_mv: ".  Cleared by each call and set when
+ * the call fails; the pointer stays valid until the thread's next call. */
 const char *row_exact_last_error(void);
 
 /* Number of kernels this process has enqueued through the library. */

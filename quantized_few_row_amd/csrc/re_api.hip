@@ -1,7 +1,8 @@
 // Host side of the row-exact mat-vec C ABI: argument checks, schedule and
-// launch.  The checks restate mlx-native 0.18.0 src/ops/row_exact_matvec.rs
-// validate() (shape, schedule, k multiple, strides and offsets, output
-// aliasing, sizes); the schedule is this library's own (wave64 pieces,
+// launch.  The argument contract is that of mlx-native 0.18.0
+// src/ops/row_exact_matvec.rs, validate() (shape, k multiple, strides,
+// pointer alignment, output aliasing, sizes), checked here in this library's
+// own order and terms; the schedule is this library's own (wave64 pieces,
 // rows per wave, LDS passes).
 #include <atomic>
 #include <cstdarg>
@@ -61,13 +62,15 @@ uint32_t k_multiple(int t) {
     }
 }
 
-// Weight pointer alignment this library needs (the page asks 8 / 2 / 16 / 2 / 2
-// for its five types; F32 rows are read 16 bytes at a time, BF16 as F16).
+// Weight pointer alignment (the page's 8 / 2 / 16 / 2 / 2 bytes for its five
+// types; F32 rows are read 16 bytes at a time, BF16 as F16).  Q8_0, Q6_K and
+// Q5_0 blocks are read with loads that never start before the block (see
+// row_base in the kernels), so 2 bytes suffice.
 uint32_t w_align(int t) {
     switch (t) {
     case kF16: case kBF16: return 8;
     case kQ4K: case kF32: return 16;
-    default: return 4;
+    default: return 2;
     }
 }
 
@@ -158,14 +161,18 @@ row_exact_strides_t resolve_strides(const row_exact_strides_t *s, uint32_t m, ui
     return c;
 }
 
-// Shape checks shared by every entry point (validate(): m, n/k/batch, k multiple).
+// Checks every entry point shares: weight type, m, the dimensions and k's
+// block multiple.  Rows are counted in 32 bits inside the kernels (row groups
+// of up to 16 rows), so n stays below 2^31.
 int check_shape(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch) {
-    if (!valid_type(t)) return fail(ROW_EXACT_EARG, "unknown weight type %d", t);
-    if (m == 0 || m > ROW_EXACT_MAX_ROWS) return fail(ROW_EXACT_EARG, "m (%u) must be in 1..=8", m);
-    if (n == 0 || k == 0 || batch == 0)
-        return fail(ROW_EXACT_EARG, "n (%u), k (%u) and batch (%u) must be > 0", n, k, batch);
+    if (!valid_type(t)) return fail(ROW_EXACT_EARG, "weight type %d is not one of 0..%d", t, kNumTypes - 1);
+    if (m < 1 || m > ROW_EXACT_MAX_ROWS)
+        return fail(ROW_EXACT_EARG, "m = %u: a call takes 1 to %d input rows", m, ROW_EXACT_MAX_ROWS);
+    if (!n || !k || !batch)
+        return fail(ROW_EXACT_EARG, "n = %u, k = %u, batch = %u: every dimension must be at least 1", n, k, batch);
     if (k % k_multiple(t))
-        return fail(ROW_EXACT_EARG, "k (%u) must be a multiple of %u for %s", k, k_multiple(t), type_name(t));
+        return fail(ROW_EXACT_EARG, "%s weights need k divisible by %u, got k = %u", type_name(t), k_multiple(t), k);
+    if (n > 0x7fffffffu) return fail(ROW_EXACT_EEXTENT, "n = %u: at most 2^31 - 1 weight rows per batch entry", n);
     return 0;
 }
 
@@ -177,7 +184,7 @@ int sizes(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, const row_e
     const u128 y = extent(batch, s.y_batch_stride, m, s.y_row_stride, n) * 4;
     const u128 lim = (u128)1 << 62;
     if (w >= lim || x >= lim || y >= lim)
-        return fail(ROW_EXACT_EEXTENT, "operand sizes overflow 64-bit byte offsets");
+        return fail(ROW_EXACT_EEXTENT, "W, x or y spans 2^62 bytes or more");
     wb = (uint64_t)w;
     xb = (uint64_t)x;
     yb = (uint64_t)y;
@@ -186,45 +193,58 @@ int sizes(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, const row_e
 
 bool overlap(uintptr_t a, uint64_t an, uintptr_t b, uint64_t bn) { return a < b + bn && b < a + an; }
 
+// Output element (b, j, i), i < n, sits at b*ybs + j*yrs + i.  Accepted
+// layouts nest: of the two strided axes that have more than one entry, the
+// one with the smaller stride is the inner one, and each stride reaches past
+// everything nested inside it (n values, then the inner axis' whole extent).
+// Every nested layout writes each element once; interleaved layouts (which
+// can also be free of collisions) are refused, as the page refuses them.
+bool outputs_nest(uint32_t n, uint32_t m, uint64_t yrs, uint32_t batch, uint64_t ybs) {
+    struct Axis { uint64_t stride; uint32_t count; } ax[2] = {{yrs, m}, {ybs, batch}};
+    if (ax[1].stride < ax[0].stride) {
+        const Axis t = ax[0];
+        ax[0] = ax[1];
+        ax[1] = t;
+    }
+    u128 span = n;
+    for (const Axis &a : ax) {
+        if (a.count < 2) continue;
+        if ((u128)a.stride < span) return false;
+        span += (u128)(a.count - 1) * a.stride;
+    }
+    return true;
+}
+
 int validate_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                 const row_exact_strides_t &s, uint64_t &wb, uint64_t &xbytes, uint64_t &ybytes,
                 const int32_t *ids = nullptr, uint32_t num_experts = 0) {
     int rc = check_shape(t, n, k, m, batch);
     if (rc) return rc;
     if (!W || !x || !y) return fail(ROW_EXACT_EARG, "W, x and y must be non-NULL device pointers");
-    if (ids && num_experts == 0) return fail(ROW_EXACT_EARG, "num_experts must be > 0");
-    if (ids && (uintptr_t)ids % 4) return fail(ROW_EXACT_EALIGN, "expert_ids must be 4-byte aligned");
-    if (s.x_row_stride % 4 || s.x_batch_stride % 4 || ((uintptr_t)x % 16))
-        return fail(s.x_row_stride % 4 || s.x_batch_stride % 4 ? ROW_EXACT_ESTRIDE : ROW_EXACT_EALIGN,
-                    "input strides (%u, %u) must be multiples of 4 and the input pointer 16-byte aligned "
-                    "(offset %u)",
-                    s.x_row_stride, s.x_batch_stride, (unsigned)((uintptr_t)x % 16));
-    if ((uintptr_t)W % w_align(t) || (uintptr_t)y % 4)
-        return fail(ROW_EXACT_EALIGN, "weight pointer (offset %u) must be %u-byte and output (offset %u) 4-byte aligned",
-                    (unsigned)((uintptr_t)W % 16), w_align(t), (unsigned)((uintptr_t)y % 4));
-    // Output elements must not alias (either layout order is accepted).
-    const uint64_t yrs = s.y_row_stride, ybs = s.y_batch_stride;
-    const bool rows_disjoint = m == 1 || yrs >= n;
-    bool ok;
-    if (batch == 1)
-        ok = rows_disjoint;
-    else if (m == 1)
-        ok = ybs >= n;
-    else if (yrs >= ybs)
-        ok = ybs >= n && (u128)yrs >= (u128)(batch - 1) * ybs + n;
-    else
-        ok = rows_disjoint && (u128)ybs >= (u128)(m - 1) * yrs + n;
-    if (!ok)
-        return fail(ROW_EXACT_EALIAS, "output strides overlap: y_row_stride %u, y_batch_stride %u, m %u, n %u, batch %u",
-                    s.y_row_stride, s.y_batch_stride, m, n, batch);
+    if (ids && !num_experts) return fail(ROW_EXACT_EARG, "num_experts is 0: expert_ids has nothing to select");
+    const uint32_t wa = w_align(t);
+    if ((uintptr_t)W % wa)
+        return fail(ROW_EXACT_EALIGN, "%s weights must sit on a %u-byte boundary (W mod %u = %u)", type_name(t), wa,
+                    wa, (unsigned)((uintptr_t)W % wa));
+    if ((uintptr_t)x % 16)
+        return fail(ROW_EXACT_EALIGN, "x must sit on a 16-byte boundary (x mod 16 = %u)", (unsigned)((uintptr_t)x % 16));
+    if ((uintptr_t)y % 4) return fail(ROW_EXACT_EALIGN, "y must sit on a 4-byte boundary");
+    if (ids && (uintptr_t)ids % 4) return fail(ROW_EXACT_EALIGN, "expert_ids must sit on a 4-byte boundary");
+    if ((s.x_row_stride | s.x_batch_stride) & 3u)
+        return fail(ROW_EXACT_ESTRIDE, "x strides (row %u, batch %u) must be multiples of 4 elements", s.x_row_stride,
+                    s.x_batch_stride);
+    if (!outputs_nest(n, m, s.y_row_stride, batch, s.y_batch_stride))
+        return fail(ROW_EXACT_EALIAS,
+                    "y layout writes some element twice (n %u, m %u at row stride %u, batch %u at batch stride %u)", n,
+                    m, s.y_row_stride, batch, s.y_batch_stride);
     rc = sizes(t, n, k, m, batch, s, wb, xbytes, ybytes, ids ? num_experts : 0);
     if (rc) return rc;
     if (row_bytes_of(t, k) > 0x7fffffffull)
-        return fail(ROW_EXACT_EEXTENT, "a weight row of %llu bytes exceeds 2^31 - 1",
+        return fail(ROW_EXACT_EEXTENT, "one weight row takes %llu bytes, more than 2^31 - 1",
                     (unsigned long long)row_bytes_of(t, k));
     if (overlap((uintptr_t)y, ybytes, (uintptr_t)W, wb) || overlap((uintptr_t)y, ybytes, (uintptr_t)x, xbytes) ||
         (ids && overlap((uintptr_t)y, ybytes, (uintptr_t)ids, 4ull * batch)))
-        return fail(ROW_EXACT_EALIAS, "output range overlaps the weight, input or expert-id range");
+        return fail(ROW_EXACT_EALIAS, "y overlaps the bytes of W, x or expert_ids");
     return 0;
 }
 
@@ -244,16 +264,39 @@ MvAttributes mv_attributes(int t) {
     }
 }
 
+// ROW_EXACT_DEBUG (print the schedule inputs; never changes numerics), read
+// once per process.
+bool debug_enabled() {
+    static const bool on = getenv("ROW_EXACT_DEBUG") != nullptr;
+    return on;
+}
+
+// VGPRs of the plain instance <t, m, nr>, asked of the runtime once per
+// instance and process (0 = unknown).
+int instance_vgprs(int t, uint32_t m, uint32_t nr) {
+    static std::atomic<int> cache[kNumTypes][ROW_EXACT_MAX_ROWS + 1][5];  // -1 after a failed query
+    const uint32_t ni = nr == 4 ? 3 : nr;
+    std::atomic<int> &slot = cache[t][m][ni];
+    int v = slot.load(std::memory_order_relaxed);
+    if (v != 0) return v > 0 ? v : 0;
+    hipFuncAttributes attr;
+    if (mv_attributes(t)(m, nr, &attr) != hipSuccess) {
+        (void)hipGetLastError();
+        slot.store(-1, std::memory_order_relaxed);
+        return 0;
+    }
+    v = attr.numRegs > 0 ? attr.numRegs : -1;
+    slot.store(v, std::memory_order_relaxed);
+    return v > 0 ? v : 0;
+}
+
 // Workgroups of a kernel instance that fit on one CU at once: VGPRs (512 per
 // SIMD lane, 4 SIMDs, waves of a workgroup spread over the SIMDs), at most 8
 // waves per SIMD, and LDS.
 int workgroups_per_cu(int t, uint32_t m, uint32_t nr, uint32_t waves, size_t lds, size_t lds_per_cu) {
-    hipFuncAttributes attr;
-    if (mv_attributes(t)(m, nr, &attr) != hipSuccess) {
-        (void)hipGetLastError();
-        return 1;
-    }
-    const int vg = attr.numRegs > 0 ? (attr.numRegs + 7) / 8 * 8 : 256;
+    const int regs = instance_vgprs(t, m, nr);
+    if (!regs) return 1;
+    const int vg = (regs + 7) / 8 * 8;
     int per_simd = 512 / vg;
     if (per_simd > 8) per_simd = 8;
     const int waves_per_simd_per_wg = (int)((waves + 3) / 4);
@@ -261,9 +304,9 @@ int workgroups_per_cu(int t, uint32_t m, uint32_t nr, uint32_t waves, size_t lds
     int by_lds = lds ? (int)(lds_per_cu / lds) : 8;
     int r = by_regs < by_lds ? by_regs : by_lds;
     if (r > 8) r = 8;
-    if (getenv("ROW_EXACT_DEBUG"))
+    if (debug_enabled())
         fprintf(stderr, "row_exact_mv: kernel %s m=%u rows/wave=%u: %d VGPRs, %d waves/SIMD, lds %zu -> %d workgroups/CU\n",
-                type_name(t), m, nr, attr.numRegs, per_simd, lds, r < 1 ? 1 : r);
+                type_name(t), m, nr, regs, per_simd, lds, r < 1 ? 1 : r);
     return r < 1 ? 1 : r;
 }
 
@@ -544,7 +587,8 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     if (grid_x > 0x7fffffffull)
         return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);
     const size_t lds = lds_bytes(t, m, k, sch.k_chunk);
-    hipError_t e = mv_launcher(t)(a, m, nr, dim3((uint32_t)grid_x), dim3(64 * sch.waves_per_workgroup), lds, stream);
+    hipError_t e =
+        mv_launcher(t)(a, m, nr, dim3((uint32_t)grid_x), dim3(64 * sch.waves_per_workgroup), lds, di.lds_max, stream);
     if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     g_launches.fetch_add(1, std::memory_order_relaxed);
     return 0;
@@ -623,13 +667,14 @@ int row_exact_dequant(row_exact_weight_t wt, const void *W, float *out, uint32_t
     if (rc) return rc;
     if (!W || !out) return fail(ROW_EXACT_EARG, "W and out must be non-NULL device pointers");
     if ((uintptr_t)W % w_align(t) || (uintptr_t)out % 4)
-        return fail(ROW_EXACT_EALIGN, "weight pointer must be %u-byte and out 4-byte aligned", w_align(t));
+        return fail(ROW_EXACT_EALIGN, "%s weights must sit on a %u-byte boundary and out on a 4-byte one",
+                    type_name(t), w_align(t));
     const u128 wb = (u128)row_bytes_of(t, k) * rows;
     const u128 ob = (u128)rows * k * 4;
     if (wb >= ((u128)1 << 62) || ob >= ((u128)1 << 62))
-        return fail(ROW_EXACT_EEXTENT, "operand sizes overflow 64-bit byte offsets");
+        return fail(ROW_EXACT_EEXTENT, "W or out spans 2^62 bytes or more");
     if (overlap((uintptr_t)out, (uint64_t)ob, (uintptr_t)W, (uint64_t)wb))
-        return fail(ROW_EXACT_EALIAS, "output range overlaps the weight range");
+        return fail(ROW_EXACT_EALIAS, "out overlaps the bytes of W");
     DqArgs a;
     a.W = (const uint8_t *)W;
     a.out = out;

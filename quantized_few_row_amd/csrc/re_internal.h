@@ -127,18 +127,21 @@ inline uint32_t pad_period(int t) {
 }
 
 // Launchers, one translation unit per weight type.
+// lds: dynamic LDS bytes of this launch; lds_max: the device's per-workgroup
+// limit (each instance's attribute is raised to it once, on its first launch
+// that needs more than 64 KB).
 typedef hipError_t (*MvLauncher)(const MvArgs &, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds,
-                                 hipStream_t s);
+                                 size_t lds_max, hipStream_t s);
 typedef hipError_t (*DqLauncher)(const DqArgs &, hipStream_t s);
 typedef hipError_t (*MvAttributes)(uint32_t m, uint32_t nr, hipFuncAttributes *attr);
 
-hipError_t launch_mv_f16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
-hipError_t launch_mv_q8_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
-hipError_t launch_mv_q4_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
-hipError_t launch_mv_q6_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
-hipError_t launch_mv_q5_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
-hipError_t launch_mv_f32(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
-hipError_t launch_mv_bf16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, hipStream_t);
+hipError_t launch_mv_f16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
+hipError_t launch_mv_q8_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
+hipError_t launch_mv_q4_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
+hipError_t launch_mv_q6_k(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
+hipError_t launch_mv_q5_0(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
+hipError_t launch_mv_f32(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
+hipError_t launch_mv_bf16(const MvArgs &, uint32_t, uint32_t, dim3, dim3, size_t, size_t, hipStream_t);
 hipError_t attributes_mv_f16(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t attributes_mv_q8_0(uint32_t, uint32_t, hipFuncAttributes *);
 hipError_t attributes_mv_q4_k(uint32_t, uint32_t, hipFuncAttributes *);

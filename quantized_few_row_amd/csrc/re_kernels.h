@@ -11,7 +11,7 @@
 //     L+128, ... in that order, so each load instruction of a wave covers
 //     adjacent bytes of the row.
 //   - A wave streams rows_per_wave (NR) rows at once: every input value read
-//     from LDS feeds NR weight rows ("nr0 rows sharing each input load").
+//     from LDS feeds all NR weight rows (the page's nr0 packing).
 //   - The m input rows of the batch are staged once per pass into LDS
 //     (padded so that the lanes' 16-byte reads hit distinct banks).
 //
@@ -40,6 +40,8 @@
 //     add produces the same bits: every output gets the same tree for every
 //     m and every packing.
 #pragma once
+
+#include <mutex>
 
 #include "re_internal.h"
 
@@ -277,6 +279,9 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
         const uint32_t B = o0 + 22 * p;
+        // B - sh is at or after R: B >= 2 when sh == 2 (R is the row's
+        // 4-byte-aligned base, or, for a first row at a 2-byte-aligned W, the
+        // row itself, where B % 4 == 2 only from block 1 on).
         const uint32_t sh = B & 3u;
         const u32x3a4 e = ldv<u32x3a4>(R, B - sh);  // covers bytes 0..7 of the block
         const uint32_t b0 = abyte(e.y, e.x, sh);     // d | qh.lo << 16
@@ -977,21 +982,29 @@ __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *c
     }
 }
 
-// Wave-uniform base (aligned down to 4 bytes) and per-lane byte offset of
-// each of a lane's rows: row0 + r for the wave's first slot, plus slot_rows
-// for the lane's slot (short rows; slot_rows = 0 with 64 lanes per row).
-// Rows past n are clamped to n - 1 (read, never stored).
+// Wave-uniform base of a row that starts at rp and the row's offset from it:
+// rp aligned down to 4 bytes, unless that falls before the first weight byte
+// Wlo (a 2-byte-aligned W, its first row): then rp itself.  The block loads
+// read at or after base + offset - 2 only where the base is 4-byte aligned
+// (Q5_0's header dwords; see Tr<kQ5_0>::load), so nothing before W is read.
+__device__ __forceinline__ void row_base(const uint8_t *Wlo, const uint8_t *rp, const uint8_t *&R, uint32_t &o0) {
+    const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
+    R = rp - lo >= Wlo ? rp - lo : rp;
+    o0 = (uint32_t)(rp - R);
+}
+
+// Wave-uniform base and per-lane byte offset of each of a lane's rows: row0 +
+// r for the wave's first slot, plus slot_rows for the lane's slot (short
+// rows; slot_rows = 0 with 64 lanes per row).  Rows past n are clamped to
+// n - 1 (read, never stored).
 template <int NR>
-__device__ __forceinline__ void row_bases(const uint8_t *Wb, uint64_t row_bytes, uint32_t n, uint32_t row0,
-                                          bool sub_wave, uint32_t slot_rows, const uint8_t *(&R)[NR],
+__device__ __forceinline__ void row_bases(const uint8_t *Wlo, const uint8_t *Wb, uint64_t row_bytes, uint32_t n,
+                                          uint32_t row0, bool sub_wave, uint32_t slot_rows, const uint8_t *(&R)[NR],
                                           uint32_t (&o0)[NR]) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         const uint32_t row = min(row0 + r, n - 1);
-        const uint8_t *rp = Wb + (uint64_t)row * row_bytes;
-        const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
-        R[r] = rp - lo;
-        o0[r] = lo;
+        row_base(Wlo, Wb + (uint64_t)row * row_bytes, R[r], o0[r]);
         if (sub_wave) o0[r] += (uint32_t)((min(row0 + slot_rows + r, n - 1) - row) * row_bytes);
     }
 }
@@ -1005,7 +1018,7 @@ __device__ __forceinline__ void load_item(const uint8_t *Wb, const MvArgs &a, ui
                                           uint32_t slot, typename Tr<T>::Raw (&raw)[NR]) {
     const uint8_t *R[NR];
     uint32_t o0[NR];
-    row_bases<NR>(Wb, a.row_bytes, a.n, (g * NR) << (6 - lpr_of<SUB>(a)), SUB, slot * NR, R, o0);
+    row_bases<NR>(a.W, Wb, a.row_bytes, a.n, (g * NR) << (6 - lpr_of<SUB>(a)), SUB, slot * NR, R, o0);
 #pragma unroll
     for (int r = 0; r < NR; ++r) raw[r] = load_walk<T>(R[r], o0[r], p, a.k);
 }
@@ -1228,7 +1241,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             zero<M, NR>(acc);
             const uint8_t *R[NR];
             uint32_t o0[NR];
-            row_bases<NR>(Wb, a.row_bytes, a.n, g * NR, false, 0, R, o0);
+            row_bases<NR>(a.W, Wb, a.row_bytes, a.n, g * NR, false, 0, R, o0);
             for (uint32_t c = 0; c < a.nchunks; ++c) {
                 const uint32_t pb = c * a.pieces_per_chunk;
                 const uint32_t pe = min(pb + a.pieces_per_chunk, a.pieces);
@@ -1260,9 +1273,10 @@ __global__ void __launch_bounds__(256) dq_kernel(const DqArgs a) {
     const uint64_t gid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
     if (gid >= (uint64_t)a.rows * a.pieces) return;
     const uint32_t r = (uint32_t)(gid / a.pieces), p = (uint32_t)(gid % a.pieces);
-    const uint8_t *rp = a.W + (uint64_t)r * a.row_bytes;
-    const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
-    const typename TR::Raw raw = TR::load(rp - lo, lo, p, a.k);
+    const uint8_t *R;
+    uint32_t o0;
+    row_base(a.W, a.W + (uint64_t)r * a.row_bytes, R, o0);
+    const typename TR::Raw raw = TR::load(R, o0, p, a.k);
     const typename TR::Pre pre = TR::prep(raw, p);
     float *o = a.out + (uint64_t)r * a.k;
 #pragma unroll
@@ -1278,22 +1292,40 @@ __global__ void __launch_bounds__(256) dq_kernel(const DqArgs a) {
 
 // ---------------------------------------------------------------- launchers
 
-template <int T, int M, int NR>
-hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    // Unconditional-load walks (see fetch_item) only for the plain 64-lane
-    // instances, where waves hold many items on the large shapes.
-    const void *fn = a.lpr_log2 < 6 ? (a.r ? (const void *)mv_kernel<T, M, NR, true, true, false>
-                                           : (const void *)mv_kernel<T, M, NR, true, false, false>)
-                   : a.r            ? (const void *)mv_kernel<T, M, NR, false, true, false>
-                   : a.walk_unconditional ? (const void *)mv_kernel<T, M, NR, false, false, true>
-                                          : (const void *)mv_kernel<T, M, NR, false, false, false>;
-    if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+// Raises fn's dynamic-LDS limit to lds_max once per process (the first launch
+// of an instance that needs more than 64 KB), so that concurrent launches of
+// one instance never lower it under each other.
+template <int T, int M, int NR, bool SUB, bool NORM, bool UNC>
+hipError_t allow_lds(size_t lds, size_t lds_max) {
+    static std::once_flag once;
+    static hipError_t err = hipSuccess;
+    if (lds <= 65536) return hipSuccess;
+    std::call_once(once, [&] {
+        err = hipFuncSetAttribute((const void *)mv_kernel<T, M, NR, SUB, NORM, UNC>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+    });
+    return err;
+}
+
+template <int T, int M, int NR, bool SUB, bool NORM, bool UNC>
+hipError_t launch_instance(const MvArgs &a, dim3 grid, dim3 block, size_t lds, size_t lds_max, hipStream_t s) {
+    const hipError_t e = allow_lds<T, M, NR, SUB, NORM, UNC>(lds, lds_max);
+    if (e != hipSuccess) return e;
     MvArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchKernel(fn, grid, block, args, lds, s);
+    return hipLaunchKernel((const void *)mv_kernel<T, M, NR, SUB, NORM, UNC>, grid, block, args, lds, s);
+}
+
+template <int T, int M, int NR>
+hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, size_t lds_max, hipStream_t s) {
+    // Unconditional-load walks (see fetch_item) only for the plain 64-lane
+    // instances, where waves hold many items on the large shapes.
+    if (a.lpr_log2 < 6)
+        return a.r ? launch_instance<T, M, NR, true, true, false>(a, grid, block, lds, lds_max, s)
+                   : launch_instance<T, M, NR, true, false, false>(a, grid, block, lds, lds_max, s);
+    if (a.r) return launch_instance<T, M, NR, false, true, false>(a, grid, block, lds, lds_max, s);
+    if (a.walk_unconditional) return launch_instance<T, M, NR, false, false, true>(a, grid, block, lds, lds_max, s);
+    return launch_instance<T, M, NR, false, false, false>(a, grid, block, lds, lds_max, s);
 }
 
 template <int T, int M, int NR>
@@ -1327,26 +1359,27 @@ hipError_t attributes_mv(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {
 }
 
 template <int T, int M>
-hipError_t launch_m(const MvArgs &a, uint32_t nr, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+hipError_t launch_m(const MvArgs &a, uint32_t nr, dim3 grid, dim3 block, size_t lds, size_t lds_max, hipStream_t s) {
     switch (nr) {
-    case 1: return launch_one<T, M, 1>(a, grid, block, lds, s);
-    case 2: return launch_one<T, M, 2>(a, grid, block, lds, s);
-    case 4: return launch_one<T, M, 4>(a, grid, block, lds, s);
+    case 1: return launch_one<T, M, 1>(a, grid, block, lds, lds_max, s);
+    case 2: return launch_one<T, M, 2>(a, grid, block, lds, lds_max, s);
+    case 4: return launch_one<T, M, 4>(a, grid, block, lds, lds_max, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int T>
-hipError_t launch_mv(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+hipError_t launch_mv(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds, size_t lds_max,
+                     hipStream_t s) {
     switch (m) {
-    case 1: return launch_m<T, 1>(a, nr, grid, block, lds, s);
-    case 2: return launch_m<T, 2>(a, nr, grid, block, lds, s);
-    case 3: return launch_m<T, 3>(a, nr, grid, block, lds, s);
-    case 4: return launch_m<T, 4>(a, nr, grid, block, lds, s);
-    case 5: return launch_m<T, 5>(a, nr, grid, block, lds, s);
-    case 6: return launch_m<T, 6>(a, nr, grid, block, lds, s);
-    case 7: return launch_m<T, 7>(a, nr, grid, block, lds, s);
-    case 8: return launch_m<T, 8>(a, nr, grid, block, lds, s);
+    case 1: return launch_m<T, 1>(a, nr, grid, block, lds, lds_max, s);
+    case 2: return launch_m<T, 2>(a, nr, grid, block, lds, lds_max, s);
+    case 3: return launch_m<T, 3>(a, nr, grid, block, lds, lds_max, s);
+    case 4: return launch_m<T, 4>(a, nr, grid, block, lds, lds_max, s);
+    case 5: return launch_m<T, 5>(a, nr, grid, block, lds, lds_max, s);
+    case 6: return launch_m<T, 6>(a, nr, grid, block, lds, lds_max, s);
+    case 7: return launch_m<T, 7>(a, nr, grid, block, lds, lds_max, s);
+    case 8: return launch_m<T, 8>(a, nr, grid, block, lds, lds_max, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -4,8 +4,9 @@
 
 namespace rex {
 
-hipError_t launch_mv_f32(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    return launch_mv<kF32>(a, m, nr, grid, block, lds, s);
+hipError_t launch_mv_f32(const MvArgs &a, uint32_t m, uint32_t nr, dim3 grid, dim3 block, size_t lds,
+                         size_t lds_max, hipStream_t s) {
+    return launch_mv<kF32>(a, m, nr, grid, block, lds, lds_max, s);
 }
 
 hipError_t attributes_mv_f32(uint32_t m, uint32_t nr, hipFuncAttributes *attr) {

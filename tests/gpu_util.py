@@ -2,6 +2,9 @@
 compare with the oracle."""
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -63,13 +66,50 @@ def check_tolerance(got: np.ndarray, ref: np.ndarray, absum: np.ndarray, what: s
     return float((err / lim).max()) if err.size else 0.0
 
 
-def oracle_sampled(t, W: np.ndarray, x: np.ndarray, n: int, k: int, m: int, batch: int, xrs: int, xbs: int,
-                   rows: list) -> tuple:
-    """Oracle outputs for the given output rows only; returns (y, a) [batch, m, len(rows)]."""
-    ys = np.empty((batch, m, len(rows)))
-    as_ = np.empty((batch, m, len(rows)))
-    for c, i in enumerate(rows):
-        y, a = oracle.matvec(t, W, x, n, k, m, batch, xrs, xbs, rows=(i, i + 1))
-        ys[:, :, c] = y[:, :, i]
-        as_[:, :, c] = a[:, :, i]
-    return ys, as_
+def host_threads() -> int:
+    """Host threads for oracle work: the CPUs this process may use, at most
+    one GPU's share of the box (16)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return max(1, min(avail, 16))
+
+
+def _ranges(n: int, parts: int) -> list:
+    parts = max(1, min(parts, n))
+    return [(n * i // parts, n * (i + 1) // parts) for i in range(parts)]
+
+
+def oracle_full(t, W: np.ndarray, x: np.ndarray, n: int, k: int, m: int, batch: int, xrs: int, xbs: int) -> tuple:
+    """The oracle over every output row, ``(y, a)`` [batch, m, n]: the
+    unchanged oracle called on disjoint output-row ranges from several host
+    threads (each call computes its rows exactly as one call over all rows
+    would; the calls run outside the interpreter lock)."""
+    y = np.empty((batch, m, n))
+    a = np.empty((batch, m, n))
+
+    def work(r):
+        lo, hi = r
+        yy, aa = oracle.matvec(t, W, x, n, k, m, batch, xrs, xbs, rows=(lo, hi))
+        y[..., lo:hi] = yy[..., lo:hi]
+        a[..., lo:hi] = aa[..., lo:hi]
+
+    with ThreadPoolExecutor(host_threads()) as ex:
+        list(ex.map(work, _ranges(n, 4 * host_threads())))
+    return y, a
+
+
+def oracle_dequant_rows(t, W: np.ndarray, r0: int, r1: int, k: int) -> np.ndarray:
+    """The oracle's exact weights of rows [r0, r1), over host threads."""
+    rb = oracle.row_bytes(t, k)
+    flat = W.ravel()
+    out = np.empty((r1 - r0, k), dtype=np.float32)
+
+    def work(r):
+        lo, hi = r
+        out[lo - r0:hi - r0] = oracle.dequant(t, flat[lo * rb:hi * rb], hi - lo, k)
+
+    with ThreadPoolExecutor(host_threads()) as ex:
+        list(ex.map(lambda r: work((r0 + r[0], r0 + r[1])), _ranges(r1 - r0, 2 * host_threads())))
+    return out

@@ -54,7 +54,7 @@ def test_write_traffic_scales_counters_by_the_copy(counters, monkeypatch, tmp_pa
     d = counters
     bench.write_traffic(str(d / "f"), str(d / "w"), str(d / "cf"), str(d / "cw"), bench.copy_calibration_bytes(256))
     rec = json.load(open(out_root / "profiles" / "traffic.json"))
-    assert rec["kernel_source_hash"] == "abc"
+    assert all(e["kernel_source_hash"] == "abc" for e in rec["launches"].values())
     assert rec["copy_calibration"]["fetch_factor"] == pytest.approx(0.5)
     assert rec["copy_calibration"]["write_factor"] == pytest.approx(1.0)
     l1, l8 = rec["launches"]["q8_0_4096x4096:m1"], rec["launches"]["q8_0_4096x4096:m8"]
@@ -69,6 +69,21 @@ def test_write_traffic_scales_counters_by_the_copy(counters, monkeypatch, tmp_pa
     assert bench.measured_traffic("q8_0_4096x4096", 8) == l8["hbm_bytes"]
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "other")
     assert bench.measured_traffic("q8_0_4096x4096", 8) is None
+    # a record for another workload, taken later on other sources, leaves the
+    # first workload's entries in place with their own hash
+    bench.write_traffic(str(d / "f"), str(d / "w"), str(d / "cf"), str(d / "cw"), bench.copy_calibration_bytes(256),
+                        workload="q8_0_4096x4096_add_rmsnorm")
+    rec = json.load(open(out_root / "profiles" / "traffic.json"))
+    assert rec["launches"]["q8_0_4096x4096:m8"]["kernel_source_hash"] == "abc"
+    assert rec["launches"]["q8_0_4096x4096_add_rmsnorm:m8"]["kernel_source_hash"] == "other"
+    assert bench.measured_traffic("q8_0_4096x4096_add_rmsnorm", 8) is not None
+    assert bench.measured_traffic("q8_0_4096x4096", 8) is None
+
+
+def test_host_threads_stay_within_one_gpu_share():
+    threads, avail = bench.host_threads()
+    assert 1 <= threads <= bench.HOST_THREADS_PER_GPU and threads <= avail
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
 
 
 def test_copy_calibration_size_is_whole_vectors():

@@ -101,31 +101,35 @@ def _mv(wt=Weight.Q8_0, W=WP, x=XP, y=YP, n=64, k=256, m=4, batch=1, strides=Non
 
 
 @pytest.mark.parametrize("kw,code,text", [
-    (dict(m=0), -1, "m (0) must be in 1..=8"),
-    (dict(m=9), -1, "m (9) must be in 1..=8"),
-    (dict(n=0), -1, "must be > 0"),
-    (dict(k=0), -1, "must be > 0"),
-    (dict(batch=0), -1, "must be > 0"),
-    (dict(wt=7), -1, "unknown weight type"),
-    (dict(wt=-1), -1, "unknown weight type"),
-    (dict(wt=Weight.Q8_0, k=48), -1, "multiple of 32"),
-    (dict(wt=Weight.Q4_K, k=512 + 32), -1, "multiple of 256"),
-    (dict(wt=Weight.Q6_K, k=128), -1, "multiple of 256"),
-    (dict(wt=Weight.Q5_0, k=16), -1, "multiple of 32"),
-    (dict(wt=Weight.F16, k=6), -1, "multiple of 4"),
-    (dict(wt=Weight.F32, k=10), -1, "multiple of 4"),
-    (dict(wt=Weight.BF16, k=2), -1, "multiple of 4"),
+    (dict(m=0), -1, "m = 0: a call takes 1 to 8 input rows"),
+    (dict(m=9), -1, "m = 9: a call takes 1 to 8 input rows"),
+    (dict(n=0), -1, "every dimension must be at least 1"),
+    (dict(k=0), -1, "every dimension must be at least 1"),
+    (dict(batch=0), -1, "every dimension must be at least 1"),
+    (dict(wt=7), -1, "weight type 7 is not one of"),
+    (dict(wt=-1), -1, "weight type -1 is not one of"),
+    (dict(wt=Weight.Q8_0, k=48), -1, "divisible by 32"),
+    (dict(wt=Weight.Q4_K, k=512 + 32), -1, "divisible by 256"),
+    (dict(wt=Weight.Q6_K, k=128), -1, "divisible by 256"),
+    (dict(wt=Weight.Q5_0, k=16), -1, "divisible by 32"),
+    (dict(wt=Weight.F16, k=6), -1, "divisible by 4"),
+    (dict(wt=Weight.F32, k=10), -1, "divisible by 4"),
+    (dict(wt=Weight.BF16, k=2), -1, "divisible by 4"),
+    (dict(n=1 << 31), -5, "at most 2^31 - 1 weight rows"),
+    (dict(n=0xFFFFFFFF), -5, "at most 2^31 - 1 weight rows"),
     (dict(W=0), -1, "non-NULL"),
     (dict(y=0), -1, "non-NULL"),
-    (dict(x=XP + 4), -2, "16-byte aligned"),
+    (dict(x=XP + 4), -2, "x must sit on a 16-byte boundary"),
     (dict(strides=Strides(258, 0, 64, 0)), -3, "multiples of 4"),
     (dict(strides=Strides(256, 2, 64, 0), batch=2), -3, "multiples of 4"),
     (dict(wt=Weight.Q4_K, W=WP + 4), -2, "16-byte"),
     (dict(wt=Weight.F16, W=WP + 4, k=64), -2, "8-byte"),
     (dict(wt=Weight.BF16, W=WP + 4, k=64), -2, "8-byte"),
     (dict(wt=Weight.F32, W=WP + 8, k=64), -2, "16-byte"),
-    (dict(wt=Weight.Q8_0, W=WP + 2), -2, "4-byte"),
-    (dict(y=YP + 2), -2, "4-byte aligned"),
+    (dict(wt=Weight.Q8_0, W=WP + 1), -2, "2-byte"),
+    (dict(wt=Weight.Q6_K, W=WP + 3), -2, "2-byte"),
+    (dict(wt=Weight.Q5_0, W=WP + 5), -2, "2-byte"),
+    (dict(y=YP + 2), -2, "y must sit on a 4-byte boundary"),
 ])
 def test_invalid_arguments(kw, code, text):
     before = qfr.row_exact_launch_count()
@@ -135,33 +139,60 @@ def test_invalid_arguments(kw, code, text):
     assert qfr.row_exact_launch_count() == before
 
 
-@pytest.mark.parametrize("m,n,batch,s,ok", [
-    # batch 1: rows need y_row_stride >= n (or m == 1)
-    (4, 64, 1, Strides(256, 0, 63, 0), False),
-    (1, 64, 1, Strides(256, 0, 0, 0), None),
+@pytest.mark.parametrize("wt,k", [(Weight.Q8_0, 256), (Weight.Q6_K, 512), (Weight.Q5_0, 256)])
+def test_two_byte_aligned_weights_pass_the_alignment_check(wt, k):
+    # the page's validate() asks 2-byte alignment of these three types; the
+    # call is refused afterwards for an unrelated reason (y overlapping W),
+    # which shows the alignment was accepted
+    for off in (2, 6, 10, 14):
+        rc, msg = _mv(wt=wt, W=WP + off, y=WP + 64, k=k)
+        assert rc == -4 and "y overlaps the bytes of W" in msg, (off, msg)
+
+
+# Output layouts: element (b, j, i) at b*y_batch_stride + j*y_row_stride + i.
+@pytest.mark.parametrize("m,n,batch,s", [
+    # batch 1: rows need y_row_stride >= n
+    (4, 64, 1, Strides(256, 0, 63, 0)),
+    (2, 64, 1, Strides(256, 0, 0, 0)),
     # m == 1, batch > 1: batches need y_batch_stride >= n
-    (1, 64, 3, Strides(256, 256, 0, 63), False),
-    # y_row_stride >= y_batch_stride: token-major, rows span every batch
-    (2, 64, 3, Strides(256, 256, 191, 64), False),
-    (2, 64, 3, Strides(256, 256, 192, 63), False),
-    # y_batch_stride > y_row_stride: batch-major
-    (3, 64, 2, Strides(256, 1024, 64, 191), False),
-    (3, 64, 2, Strides(256, 1024, 63, 1000), False),
+    (1, 64, 3, Strides(256, 256, 0, 63)),
+    # token-major (row stride larger): rows must clear every batch entry
+    (2, 64, 3, Strides(256, 256, 191, 64)),
+    (2, 64, 3, Strides(256, 256, 192, 63)),
+    # batch-major (batch stride larger)
+    (3, 64, 2, Strides(256, 1024, 64, 191)),
+    (3, 64, 2, Strides(256, 1024, 63, 1000)),
+    # equal strides with two entries on both axes never nest
+    (2, 64, 2, Strides(256, 256, 512, 512)),
+    # interleaved rows and entries: n = 1, elements j*3 + b*2 are
+    # {0, 2, 4, 3, 5, 7}, all distinct, but the layout does not nest, and the
+    # page's rule refuses it too
+    (2, 1, 3, Strides(256, 256, 3, 2)),
 ])
-def test_output_alias_rules(m, n, batch, s, ok):
-    # ok=None marks shapes that are valid: they are not called here (a valid
-    # call would reach the device); only the rejected ones are exercised.
-    if ok is None:
-        return
+def test_output_layouts_that_do_not_nest_are_refused(m, n, batch, s):
     rc, msg = _mv(m=m, n=n, batch=batch, strides=s)
-    assert rc == -4 and "output strides overlap" in msg, msg
+    assert rc == -4 and "writes some element twice" in msg, msg
+
+
+@pytest.mark.parametrize("m,n,batch,s", [
+    (1, 64, 1, Strides(256, 0, 0, 0)),           # one row: its stride is irrelevant
+    (4, 64, 1, Strides(256, 0, 64, 0)),          # contiguous rows
+    (1, 64, 3, Strides(256, 256, 0, 64)),        # one row per entry, entries back to back
+    (2, 64, 3, Strides(256, 256, 192, 64)),      # token-major, tight
+    (3, 64, 2, Strides(256, 1024, 64, 192)),     # batch-major, tight
+    (2, 64, 3, Strides(256, 256, 1 << 20, 64)),  # token-major, loose
+])
+def test_nested_output_layouts_pass_the_layout_check(m, n, batch, s):
+    # refused afterwards only because y overlaps W (a different message)
+    rc, msg = _mv(m=m, n=n, batch=batch, strides=s, y=WP + 64)
+    assert rc == -4 and "y overlaps the bytes of W" in msg, msg
 
 
 def test_output_must_not_overlap_inputs():
     rc, msg = _mv(y=WP + 64)
-    assert rc == -4 and "overlaps" in msg
+    assert rc == -4 and "y overlaps the bytes of W" in msg
     rc, msg = _mv(y=XP + 1024)
-    assert rc == -4 and "overlaps" in msg
+    assert rc == -4 and "y overlaps the bytes of W" in msg
 
 
 @pytest.mark.parametrize("sched,text", [
@@ -197,6 +228,11 @@ def test_dequant_validation():
     assert lib.row_exact_dequant(2, WP + 4, YP, 4, 256, None) == -2
     assert lib.row_exact_dequant(1, WP, WP + 8, 4, 64, None) == -4
     assert lib.row_exact_dequant(9, WP, YP, 4, 64, None) == -1
+    # 2-byte-aligned Q8_0 / Q6_K / Q5_0 rows pass the alignment check (then
+    # refused: out overlaps W), a 1-byte offset does not
+    for wt, k in ((1, 64), (3, 256), (4, 64)):
+        assert lib.row_exact_dequant(wt, WP + 2, WP + 8, 4, k, None) == -4
+        assert lib.row_exact_dequant(wt, WP + 1, YP, 4, k, None) == -2
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -235,10 +271,10 @@ def _gather(ids=XP + 0x100000, num_experts=4, W=WP, x=XP, y=YP, n=64, k=256, m=2
 @pytest.mark.parametrize("kw,code,text", [
     (dict(ids=0), -1, "expert_ids"),
     (dict(num_experts=0), -1, "num_experts"),
-    (dict(ids=XP + 0x100002), -2, "4-byte aligned"),
-    (dict(ids=YP + 8), -4, "expert-id"),
-    (dict(m=0), -1, "m (0)"),
-    (dict(wt=9), -1, "unknown weight type"),
+    (dict(ids=XP + 0x100002), -2, "expert_ids must sit on a 4-byte boundary"),
+    (dict(ids=YP + 8), -4, "expert_ids"),
+    (dict(m=0), -1, "m = 0"),
+    (dict(wt=9), -1, "weight type 9"),
 ])
 def test_gather_invalid_arguments(kw, code, text):
     before = qfr.row_exact_launch_count()
@@ -254,7 +290,7 @@ def test_gather_weight_extent_counts_expert_sets():
     rb = qfr.row_exact_row_bytes(Weight.Q8_0, 256)
     y = WP + 4 * 64 * rb
     rc, msg = _gather(num_experts=5, y=y, ids=XP + 0x100000)
-    assert rc == -4 and "overlaps" in msg
+    assert rc == -4 and "y overlaps the bytes of W" in msg
 
 
 RP, GP, HP = 0x7F3000000000, 0x7F4000000000, 0x7F5000000000
@@ -278,7 +314,7 @@ def _norm(r=RP, g=GP, h=HP, eps=1e-5, x=XP, y=YP, W=WP, n=64, k=256, m=4, wt=Wei
     (dict(h=RP), -4, "h overlaps"),
     (dict(h=YP), -4, "overlap"),
     (dict(r=YP), -4, "overlaps"),
-    (dict(m=9), -1, "m (9)"),
+    (dict(m=9), -1, "m = 9"),
 ])
 def test_add_rmsnorm_invalid_arguments(kw, code, text):
     before = qfr.row_exact_launch_count()

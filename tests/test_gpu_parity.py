@@ -217,3 +217,39 @@ def test_stream_read_probe_runs_every_shape():
         qfr.row_exact_stream_read(buf, buf.numel() // 16 * 16, sink, shape)
     torch.cuda.synchronize()
     assert qfr.row_exact_launch_count() == before + qfr.row_exact_stream_read_shapes()
+
+
+# The page's validate() accepts Q8_0, Q6_K and Q5_0 weights at any even
+# address.  W at a 2-byte offset (the first row then starts 2 bytes past a
+# 4-byte boundary and is read from its own start): dequant bit-exact, every
+# output against the oracle at every m, row exactness, and the same bits as
+# W at an aligned address, for the default and a multi-pass schedule.
+TWO_BYTE = [wl.Q8_0, wl.Q6_K, wl.Q5_0]
+
+
+@pytest.mark.parametrize("t", TWO_BYTE, ids=[wl.TYPE_NAMES[t] for t in TWO_BYTE])
+@pytest.mark.parametrize("off", [2, 6, 14])
+def test_two_byte_aligned_weights(t, off, data):
+    d = data[t]
+    n, k = d["n"], d["k"]
+    raw = d["W"].ravel()
+    buf = torch.zeros(raw.size + 32, dtype=torch.uint8, device="cuda:0")
+    buf[off:off + raw.size].copy_(torch.from_numpy(raw.copy()))
+    Wo = buf[off:off + raw.size]
+    assert Wo.data_ptr() % 4 == 2 and Wo.data_ptr() % 16 == off
+    out = torch.full((n, k), float("nan"), dtype=torch.float32, device="cuda:0")
+    qfr.row_exact_dequant(t, Wo, out, n, k)
+    torch.cuda.synchronize()
+    ref = oracle.dequant(t, d["W"], n, k)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    ones = [bits(run_mv(t, Wo, d["xd"][j * k:], n, k, 1)) for j in range(8)]
+    step = {wl.Q8_0: 2048, wl.Q6_K: 4096, wl.Q5_0: 2048}[t]
+    for m in range(1, 9):
+        y = run_mv(t, Wo, d["xd"], n, k, m)
+        check_tolerance(y.cpu().numpy().reshape(m, n), d["y"][:m], d["a"][:m], f"off={off} m={m}")
+        yb = bits(y).reshape(m, n)
+        for j in range(m):
+            assert np.array_equal(yb[j], ones[j]), f"m={m} row {j} differs from its m=1 result"
+        assert np.array_equal(bits(y), bits(run_mv(t, d["Wd"], d["xd"], n, k, m))), "differs from aligned W"
+        multi = bits(run_mv(t, Wo, d["xd"], n, k, m, schedule=Schedule(1, 2, 8, 4, step)))
+        assert np.array_equal(multi, bits(y)), "multi-pass schedule changed the bits"

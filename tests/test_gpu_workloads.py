@@ -1,7 +1,9 @@
 """The synthetic workloads at full size, in the launch configuration the
-benchmark times (the default schedule).  The oracle checks sampled output
-rows (first, last and seeded random ones) and sampled weight rows; row
-exactness and repeatability are checked on every output, GPU against GPU.
+benchmark times (the default schedule).  Every output of every m of each
+workload is compared with the oracle (the oracle split by output rows over
+host threads), every weight row's dequantized values are compared bit for
+bit, and row exactness and repeatability are checked on every output, GPU
+against GPU.
 """
 import numpy as np
 import pytest
@@ -10,7 +12,7 @@ import torch
 import oracle
 import quantized_few_row_amd as qfr
 import workloads as wl
-from gpu_util import bits, check_tolerance, oracle_sampled, run_mv, to_dev
+from gpu_util import bits, check_tolerance, oracle_dequant_rows, oracle_full, run_mv, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -19,11 +21,20 @@ NORM_NAMES = [w.name for w in wl.WORKLOADS if w.fused_norm]
 GATHER_NAMES = [w.name for w in wl.WORKLOADS if w.experts]
 
 
-def _sample_rows(n, count=24, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = {0, 1, n // 2, n - 2, n - 1}
-    rows |= set(rng.integers(0, n, count).tolist())
-    return sorted(r for r in rows if 0 <= r < n)
+def check_all_weights(t, W, Wd, n, k, chunk_values=1 << 26):
+    """row_exact_dequant of every weight row, bit-exact against the oracle,
+    in chunks of rows."""
+    rb = qfr.row_exact_row_bytes(t, k)
+    step = max(1, chunk_values // k)
+    out = torch.empty((min(step, n), k), dtype=torch.float32, device="cuda:0")
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        qfr.row_exact_dequant(t, Wd.data_ptr() + r0 * rb, out, r1 - r0, k)
+        torch.cuda.synchronize()
+        got = out[:r1 - r0].cpu().numpy()
+        ref = oracle_dequant_rows(t, W, r0, r1, k)
+        bad = np.argwhere(got.view(np.uint32) != ref.view(np.uint32))
+        assert bad.size == 0, f"weight rows {r0}..{r1}: {bad.shape[0]} values differ, first at {bad[0].tolist()}"
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -35,16 +46,9 @@ def test_full_size_workload(name):
     x = w.make_x(8)
     Wd = to_dev(W.ravel())
     xd = to_dev(x.ravel())
-    rows = _sample_rows(n, seed=w.index)
-    rb = qfr.row_exact_row_bytes(t, k)
 
-    # dequantized weights, sampled rows, bit-exact
-    for r in rows[:8]:
-        out = torch.empty((1, k), dtype=torch.float32, device="cuda:0")
-        qfr.row_exact_dequant(t, Wd.data_ptr() + r * rb, out, 1, k)
-        torch.cuda.synchronize()
-        ref = oracle.dequant(t, W.ravel()[r * rb:(r + 1) * rb], 1, k)
-        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), f"weight row {r}"
+    check_all_weights(t, W, Wd, n * batch, k)
+    print(f"[workload] {name}: all {n * batch} weight rows bit-exact", flush=True)
 
     xrs, xbs, yrs, ybs = w.strides(8)
     strides = qfr.Strides(xrs, xbs, yrs, ybs)
@@ -52,13 +56,13 @@ def test_full_size_workload(name):
     for m in sorted(set(w.ms) | {1}):
         y = run_mv(t, Wd, xd, n, k, m, batch, strides=strides)
         yc = y.cpu().numpy()
-        ref, a = oracle_sampled(t, W, x.ravel(), n, k, m, batch, xrs, xbs, rows)
+        ref, a = oracle_full(t, W, x.ravel(), n, k, m, batch, xrs, xbs)
         got = np.empty_like(ref)
         for b in range(batch):
             for j in range(m):
-                got[b, j] = yc[b * ybs + j * yrs + np.array(rows)]
+                got[b, j] = yc[b * ybs + j * yrs:b * ybs + j * yrs + n]
         ratio = check_tolerance(got, ref, a, f"{name} m={m}")
-        print(f"[workload] {name} m={m}: sampled {len(rows)} rows x {batch} batches ok, "
+        print(f"[workload] {name} m={m}: all {batch} x {m} x {n} outputs within tolerance, "
               f"worst |err|/bound = {ratio:.3g}", flush=True)
         ybits = bits(y)
         if m == 1:

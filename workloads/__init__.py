@@ -232,7 +232,13 @@ WORKLOADS: List[Workload] = [
     Workload("q4_k_moe_64x1408x2048_top8", Q4_K, 1408, 2048, 8, (1, 4, 8), 8, experts=64),
     # the Q8_0 projection with its input made by the fused add + RMS norm (eps 1e-5)
     Workload("q8_0_4096x4096_add_rmsnorm", Q8_0, 4096, 4096, 1, (1, 4, 8), 9, fused_norm=True),
+    # held-out shapes: never used to tune the schedule chooser; the decode
+    # shapes the row-exact page reports measurements for (Q4_K 1024 x 2816,
+    # Q8_0 2816 x 2112, rows x k, m = 1..4)
+    Workload("q4_k_1024x2816", Q4_K, 1024, 2816, 1, (1, 2, 3, 4), 10),
+    Workload("q8_0_2816x2112", Q8_0, 2816, 2112, 1, (1, 2, 3, 4), 11),
 ]
+HELD_OUT = ("q4_k_1024x2816", "q8_0_2816x2112")
 BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
 
 
