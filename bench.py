@@ -635,8 +635,10 @@ def schedule_sweep(path, names=None):
             y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
             d = qfr.row_exact_schedule(t, n, k, m, batch)
             cands = {}
+            # one pass, the default's pass length, half of it and one wave step
+            kcs = {k, d.k_chunk, max(step[t], d.k_chunk // 2 // step[t] * step[t]), step[t]}
             for nr, wv, f in itertools.product((1, 2, 4), (2, 4, 8), (1, 2, 4, 8, 16, 32, 0)):
-                for kc in (k, k // 2):
+                for kc in sorted(kcs):
                     if kc < k and kc % step[t]:
                         continue
                     wgs = max(1, cus * f // wv // batch) if f else 1 << 30

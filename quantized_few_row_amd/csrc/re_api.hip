@@ -310,6 +310,31 @@ int workgroups_per_cu(int t, uint32_t m, uint32_t nr, uint32_t waves, size_t lds
     return r < 1 ? 1 : r;
 }
 
+// Waves per workgroup: 8, halved while the row groups would leave waves of
+// the device without one, but never fewer than stage the workgroup's m*kc/4
+// chunks of x with at most two loads per thread: waves without rows still
+// stage x (held-out Q4_K 1024 x 2816, m = 1..4: 8 waves, half of them
+// without rows, 3-6% faster than 4 busy waves; F16 256 x 512 at m = 1, 2 KB
+// of x: one wave, 7% faster than 8).
+uint32_t waves_per_workgroup(uint32_t gpb, uint32_t batch, int cus, uint32_t m, uint32_t kc) {
+    uint32_t w = 8;
+    while (w > 1 && (uint64_t)gpb * batch < (uint64_t)w * cus) w >>= 1;
+    const uint64_t chunks = (uint64_t)m * kc / 4;
+    uint32_t wx = 1;
+    while (wx < 8 && (uint64_t)wx * 64 * 2 < chunks) wx <<= 1;
+    return w > wx ? w : wx;
+}
+
+// Most workgroups per batch entry worth launching for gpb row groups: one
+// row group per wave, or, when that leaves CUs without a workgroup, one per
+// CU while there are row groups (its waves without rows only stage x).
+uint32_t max_workgroups(uint32_t gpb, uint32_t waves, uint32_t batch, int cus) {
+    const uint32_t by_waves = (gpb + waves - 1) / waves;
+    const uint32_t per_cu = (uint32_t)(((uint64_t)cus + batch - 1) / batch);
+    const uint32_t by_cus = gpb < per_cu ? gpb : per_cu;
+    return by_waves > by_cus ? by_waves : by_cus;
+}
+
 // Most rows per wave whose kernel holds all its state in registers at this m.
 uint32_t max_rows_per_wave(int t, uint32_t m) {
     if ((t == kQ4K || t == kQ6K) && m >= 5) return 2;
@@ -363,10 +388,9 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         s.rows_per_wave = nr;
         const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
         const uint32_t gpb = (n + rg - 1) / rg;
-        uint32_t waves = 8;
-        while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
+        const uint32_t waves = waves_per_workgroup(gpb, batch, di.cus, m, kc);
         s.waves_per_workgroup = waves;
-        const uint32_t max_wgs = (gpb + waves - 1) / waves;
+        const uint32_t max_wgs = max_workgroups(gpb, waves, batch, di.cus);
         uint64_t w = (target / waves + batch - 1) / batch;
         // as for more input rows below: no more workgroups than keep each
         // one's weight bytes at or above the m*k*4 bytes of x it stages
@@ -400,13 +424,12 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     s.rows_per_wave = nr;
     const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
     const uint32_t gpb = (n + rg - 1) / rg;
-    uint32_t waves = 8;
-    while (waves > 1 && (uint64_t)gpb * batch < (uint64_t)waves * di.cus) waves >>= 1;
+    const uint32_t waves = waves_per_workgroup(gpb, batch, di.cus, m, kc);
     s.waves_per_workgroup = waves;
     // workgroups: single pass -> as many as fit on the device at once (each
     // then walks its share of row groups); several passes -> one row group
     // per wave
-    const uint32_t max_wgs = (gpb + waves - 1) / waves;
+    const uint32_t max_wgs = max_workgroups(gpb, waves, batch, di.cus);
     uint32_t wgs;
     if (kc >= k) {
         const int per_cu = workgroups_per_cu(t, m, nr, waves, lds_bytes(t, m, k, kc), di.lds_max);
@@ -576,6 +599,17 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     a.norm_offset = (uint32_t)lds_x_bytes(t, m, k, sch.k_chunk);
     a.sx_offset = (uint32_t)lds_sx_offset(t, m, k, sch.k_chunk);
     a.sx_stride = sx_stride(t, k, sch.k_chunk);
+    // x by loads that write LDS directly where, at m = 1, it is larger than
+    // the register staging requests ahead of the weights (2 chunks of 4
+    // values per thread; the rest would be requested behind the weights, a
+    // second memory round trip before the first multiply: Q6_K 4096 x 14336
+    // -7%).  At m = 2 (4 chunks per thread ahead) the same measured 3%
+    // slower than the register staging, and elsewhere it is not needed.
+    {
+        const uint64_t ahead = 4ull * 2 * 64 * sch.waves_per_workgroup;
+        const bool dma_type = t == kQ6K;  // the types with a DMA staging path (Tr<T>::LOADS > 0)
+        a.x_dma = (a.nchunks == 1 && m == 1 && !norm && dma_type && k > ahead) ? 1u : 0u;
+    }
     {
         // items a wave walks in the single pass: its row groups x wave steps
         const uint32_t waves = sch.waves_per_workgroup;

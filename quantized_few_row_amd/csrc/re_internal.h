@@ -44,6 +44,10 @@ struct MvArgs {
     // row, at byte offset sx_offset in LDS, sx_stride floats per row.
     uint32_t sx_offset;
     uint32_t sx_stride;
+    // 1: stage x with loads that write LDS directly, all of it ahead of the
+    // weights (single pass, m = 1, x larger than the register staging
+    // requests ahead of them)
+    uint32_t x_dma;
 };
 
 struct DqArgs {

@@ -67,6 +67,11 @@
 #ifndef REX_X_FIRST_UNC_MIN_M
 #define REX_X_FIRST_UNC_MIN_M 6
 #endif
+// 1: single-pass instances of types with a fixed load count per piece stage
+// x with loads that write LDS directly (see stage_x_dma).
+#ifndef REX_X_DMA
+#define REX_X_DMA 1
+#endif
 
 
 namespace rex {
@@ -142,6 +147,8 @@ template <int T> struct Tr;
 // Piece p: values 8p..8p+7 (16 bytes).  k % 8 == 4 leaves a half piece.
 template <> struct Tr<kF16> : Geo<kF16> {
     static constexpr int SEG = 0;  // no scale: the fma chain runs on w
+    static constexpr int LOADS = 0;  // x staged in registers (a piece takes 1 or 2 loads)
+    static constexpr int ITEM_DWORDS = 4;
     struct Raw { uint32_t w[4]; };
     struct Pre {};
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t k) {
@@ -179,6 +186,8 @@ template <> struct Tr<kF16> : Geo<kF16> {
 // of a float32, so the exact widening is a 16-bit shift.
 template <> struct Tr<kBF16> : Geo<kBF16> {
     static constexpr int SEG = 0;
+    static constexpr int LOADS = 0;  // as F16
+    static constexpr int ITEM_DWORDS = 4;
     struct Raw { uint32_t w[4]; };
     struct Pre {};
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t k) {
@@ -207,6 +216,8 @@ template <> struct Tr<kBF16> : Geo<kBF16> {
 // 4k bytes with k % 4 == 0).
 template <> struct Tr<kF32> : Geo<kF32> {
     static constexpr int SEG = 0;
+    static constexpr int LOADS = 0;  // x staged in registers (see stage_x_dma)
+    static constexpr int ITEM_DWORDS = 4;
     struct Raw { uint32_t w[4]; };
     struct Pre {};
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -234,6 +245,8 @@ template <> struct Tr<kF32> : Geo<kF32> {
 // Piece p: block p (34 bytes: f16 d, 32 int8).  w = d * q.
 template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
     static constexpr int SEG = 8;  // one scale per piece
+    static constexpr int LOADS = 0;  // x staged in registers (see stage_x_dma)
+    static constexpr int ITEM_DWORDS = 9;
     struct Raw { uint32_t q[8]; uint32_t d; };
     struct Pre { float d; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -254,7 +267,7 @@ template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = pr.d * (float)(int8_t)(r.q[g] >> (8 * i));
     }
-    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+    static __device__ __forceinline__ void deqi(const Raw &r, const Pre &, int g, float (&q)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(r.q[g] >> (8 * i));
     }
@@ -274,14 +287,13 @@ template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
 // one signed-byte convert and scaled by d/8 (exact).
 template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
     static constexpr int SEG = 8;  // one scale per piece
+    static constexpr int LOADS = 0;  // x staged in registers (see stage_x_dma)
+    static constexpr int ITEM_DWORDS = 6;
     struct Raw { uint32_t qs[4]; uint32_t nqh; uint32_t d; };
     struct Pre { float d8; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
         const uint32_t B = o0 + 22 * p;
-        // B - sh is at or after R: B >= 2 when sh == 2 (R is the row's
-        // 4-byte-aligned base, or, for a first row at a 2-byte-aligned W, the
-        // row itself, where B % 4 == 2 only from block 1 on).
         const uint32_t sh = B & 3u;
         const u32x3a4 e = ldv<u32x3a4>(R, B - sh);  // covers bytes 0..7 of the block
         const uint32_t b0 = abyte(e.y, e.x, sh);     // d | qh.lo << 16
@@ -303,7 +315,7 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.d8;
     }
-    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+    static __device__ __forceinline__ void deqi(const Raw &r, const Pre &, int g, float (&q)[4]) {
         const uint32_t b = bytes8(r, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(b >> (8 * i));
@@ -326,6 +338,8 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
     // One scale and one offset per 32 values (groups 8e..8e+7, sub-block
     // 2c+e): the segment contributes d*sc * sum(q*x) - dmin*mn * sum(x).
     static constexpr int SEG = 8;
+    static constexpr int LOADS = 0;  // x staged in registers (see stage_x_dma)
+    static constexpr int ITEM_DWORDS = 12;
     struct Raw { uint32_t qs[8]; uint32_t h[4]; };
     struct Pre { float dsc[2], dmn[2]; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
@@ -366,7 +380,7 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = __builtin_fmaf(pr.dsc[e], (float)((q4 >> (8 * i)) & 0xffu), -pr.dmn[e]);
     }
-    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
+    static __device__ __forceinline__ void deqi(const Raw &r, const Pre &, int g, float (&q)[4]) {
         const uint32_t dw = r.qs[g & 7];
         const uint32_t q4 = opaque(g >= 8 ? ((dw >> 4) & 0x0F0F0F0Fu) : (dw & 0x0F0F0F0Fu));
 #pragma unroll
@@ -395,9 +409,13 @@ template <> struct Tr<kQ4K> : Geo<kQ4K> {
 // w = (d * sc) * (q - 32), exact.
 template <> struct Tr<kQ6K> : Geo<kQ6K> {
     static constexpr int SEG = 4;  // one scale per 16 values (groups 4t..4t+3)
-    // s4: the piece's four sub-scales sc[8hh + 2t + l0/16], t = 0..3, as bytes 0..3.
-    struct Raw { uint32_t ql0[4], ql1[4], qhx[4], s4, d; };
-    struct Pre { float ds4[4]; };
+    static constexpr int LOADS = 5;  // 3 x 16 bytes, 8 scale bytes, d
+    static constexpr int ITEM_DWORDS = 14;
+    // Raw: the piece's bytes as loaded (low bits, high bits, the eight scales
+    // of its half, d); Pre (at multiply time): d*sc/4 of its four 16-value
+    // segments and the high bits with the top bit of each 2-bit part inverted.
+    struct Raw { uint32_t ql0[4], ql1[4], qh[4], sc[2], d; };
+    struct Pre { float ds4[4]; uint32_t qhx[4]; };
     // Piece `pos` (0..3) of super-block sb of a row.
     static __device__ __forceinline__ Raw load_at(const uint8_t *R, uint32_t o0, uint32_t sb, uint32_t pos) {
         Raw r;
@@ -408,12 +426,10 @@ template <> struct Tr<kQ6K> : Geo<kQ6K> {
         const uint32_t B = o0 + __umul24(sb, 210u);
         load16_u(R, B + oql, r.ql0);
         load16_u(R, B + (oql + 32), r.ql1);
-        load16_u(R, B + oqh, r.qhx);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.qhx[i] ^= 0xAAAAAAAAu;  // invert bit 1 of every 2-bit high part
+        load16_u(R, B + oqh, r.qh);
         const u32x2a2 v = ldv<u32x2a2>(R, B + osc);  // sc[8hh .. 8hh+7]
-        // bytes (pos & 1) + 0, 2, 4, 6 of the eight (v_perm_b32: selector 0-3 = v.x, 4-7 = v.y)
-        r.s4 = __builtin_amdgcn_perm(v.y, v.x, 0x06040200u + 0x01010101u * (pos & 1));
+        r.sc[0] = v.x;
+        r.sc[1] = v.y;
         r.d = ld16(R, B + 208);
         return r;
     }
@@ -428,31 +444,36 @@ template <> struct Tr<kQ6K> : Geo<kQ6K> {
     static __device__ __forceinline__ Raw load_walk(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         return load_at(R, o0, p >> 2, threadIdx.x & 3u);
     }
-    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) {
+    // p: the piece (its position in the super-block, p % 4, decides which
+    // four of the eight scales are its own).
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t p) {
         Pre pr;
+        // scale bytes (p & 1) + 0, 2, 4, 6 of the eight (v_perm_b32: selector 0-3 = sc[0], 4-7 = sc[1])
+        const uint32_t s4 = __builtin_amdgcn_perm(r.sc[1], r.sc[0], 0x06040200u + 0x01010101u * (p & 1));
         const float d4 = h2f(r.d) * 0.25f;  // exact (a power of two, far from underflow)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) pr.ds4[t] = d4 * (float)(int8_t)(r.s4 >> (8 * t));  // exact: d*sc/4
+        for (int t = 0; t < 4; ++t) pr.ds4[t] = d4 * (float)(int8_t)(s4 >> (8 * t));  // exact: d*sc/4
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr.qhx[i] = r.qh[i] ^ 0xAAAAAAAAu;  // invert bit 1 of every 2-bit high part
         return pr;
     }
     // Four values at a time: byte i becomes the int8 4*(q_i - 32) (low 4
-    // bits in bits 2..5, high 2 bits in bits 6..7 with the top one inverted,
-    // the inversion applied to qh at load), converted with one signed-byte
-    // convert and scaled by d*sc/4: exactly d*sc*(q-32), sign of zero
-    // included.
-    static __device__ __forceinline__ uint32_t bytes4(const Raw &r, int g) {
+    // bits in bits 2..5, high 2 bits in bits 6..7 with the top one inverted),
+    // converted with one signed-byte convert and scaled by d*sc/4: exactly
+    // d*sc*(q-32), sign of zero included.
+    static __device__ __forceinline__ uint32_t bytes4(const Raw &r, const Pre &pr, int g) {
         const int t = g >> 2, G = g & 3;
         const uint32_t src = (t & 1) ? r.ql1[G] : r.ql0[G];
         const uint32_t lo = t < 2 ? ((src << 2) & 0x3C3C3C3Cu) : ((src >> 2) & 0x3C3C3C3Cu);
-        return ((r.qhx[G] << (6 - 2 * t)) & 0xC0C0C0C0u) | lo;
+        return ((pr.qhx[G] << (6 - 2 * t)) & 0xC0C0C0C0u) | lo;
     }
     static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
-        const uint32_t b = bytes4(r, g);
+        const uint32_t b = bytes4(r, pr, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.ds4[g >> 2];
     }
-    static __device__ __forceinline__ void deqi(const Raw &r, int g, float (&q)[4]) {
-        const uint32_t b = bytes4(r, g);
+    static __device__ __forceinline__ void deqi(const Raw &r, const Pre &pr, int g, float (&q)[4]) {
+        const uint32_t b = bytes4(r, pr, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(b >> (8 * i));
     }
@@ -678,6 +699,59 @@ __device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const floa
 #pragma unroll
         for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = *(const f32x4 *)(xb + (uint64_t)j * xrs + lv);
     }
+}
+
+// x staged by loads that write LDS directly (gfx950 global_load_lds_dwordx4:
+// lane L of a wave writes the 16 bytes it reads to lds + 16 L, no VGPRs), so
+// all of x can be requested ahead of the weights whatever its size.  Used
+// where x is larger than the register staging requests ahead of the weights
+// (see the host's x_dma), for the types whose Tr<T>::LOADS gives the fixed
+// number of load instructions of a piece (Q6_K); the others keep the
+// register staging: the extra code path cost them 1-9% at m = 1 on MI355X.  Each wave
+// instruction fills 64 consecutive 16-byte slots of one staged row in the
+// padded layout (Geo<T>::PADP values, then one pad slot); a lane reads the
+// x chunk its slot holds, pad slots and slots past the row are masked off.
+// Completion is counted by vmcnt with the other loads, in issue order: the
+// caller waits with barrier_after_loads, never with __syncthreads.
+__device__ __forceinline__ void lds_dma16(const float *src, float *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+template <int T, int M>
+__device__ __forceinline__ void stage_x_dma(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
+                                            uint32_t k, uint32_t XS, uint32_t wave, uint32_t nwaves, uint32_t lane) {
+    constexpr uint32_t P = Geo<T>::PADP / 4;  // data slots per pad period
+    const uint32_t S = XS / 4;                 // slots per staged row
+    const uint32_t bpr = (S + 63) >> 6;        // 64-slot blocks per row
+    const uint32_t n4 = k >> 2;
+    for (uint32_t t = wave; t < (uint32_t)M * bpr; t += nwaves) {
+        const uint32_t j = t / bpr, b = t - j * bpr;
+        const uint32_t s = (b << 6) + lane;
+        const uint32_t per = s / (P + 1), r = s - per * (P + 1);
+        const uint32_t d = per * P + r;
+        if (r < P && d < n4) lds_dma16(xb + (uint64_t)j * xrs + 4 * d, xs + j * XS + (b << 8));
+    }
+}
+
+// s_waitcnt immediate (gfx9 layout): vmcnt n, expcnt and lgkmcnt not waited on.
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Barrier after this wave's loads issued before its last N load
+// instructions have completed: loads complete in issue order, so the x
+// chunks staged ahead of N weight loads are in LDS, while those weight loads
+// stay in flight.  N must be the exact number of load instructions issued
+// after the staging (fewer would wait for weights; more would let the
+// barrier pass before x is in LDS: a CPU test reads the count out of the
+// built code).  The fence after the barrier is acquire-only: a release
+// fence would make the compiler wait for every load in flight (it counts
+// the LDS-writing loads as outstanding LDS stores), and without any fence it
+// was free to regroup the walk's weight loads ahead of their multiplies
+// (then each step waited for all of them).
+template <int N> __device__ __forceinline__ void barrier_after_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(N));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 // Segment sums of the staged input (offset types): sx[j*SXS + s] = the sum
@@ -924,7 +998,7 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 float q[4];
-                TR::deqi(raw[r], g, q);
+                TR::deqi(raw[r], pre[r], g, q);
 #pragma unroll
                 for (int j = 0; j < M; ++j) {
 #pragma unroll
@@ -984,13 +1058,16 @@ __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *c
 
 // Wave-uniform base of a row that starts at rp and the row's offset from it:
 // rp aligned down to 4 bytes, unless that falls before the first weight byte
-// Wlo (a 2-byte-aligned W, its first row): then rp itself.  The block loads
-// read at or after base + offset - 2 only where the base is 4-byte aligned
-// (Q5_0's header dwords; see Tr<kQ5_0>::load), so nothing before W is read.
+// Wlo: then rp itself.  W and every row start are 2-byte aligned, so that
+// happens exactly for the first row of a W 2 bytes past a 4-byte boundary
+// (a scalar 64-bit equality; an ordered 64-bit compare would take vector
+// instructions).  The block loads read at or after base + offset - 2 only
+// where the base is 4-byte aligned (Q5_0's header dwords; see
+// Tr<kQ5_0>::load), so nothing before W is read.
 __device__ __forceinline__ void row_base(const uint8_t *Wlo, const uint8_t *rp, const uint8_t *&R, uint32_t &o0) {
     const uint32_t lo = (uint32_t)(uintptr_t)rp & 3u;
-    R = rp - lo >= Wlo ? rp - lo : rp;
-    o0 = (uint32_t)(rp - R);
+    o0 = rp == Wlo ? 0u : lo;
+    R = rp - o0;
 }
 
 // Wave-uniform base and per-lane byte offset of each of a lane's rows: row0 +
@@ -1044,10 +1121,11 @@ template <int M, int NR> __device__ __forceinline__ void zero(float (&acc)[NR][M
 }
 
 // Items in flight ahead of the one being multiplied (1 or 2), chosen so the
-// raw buffers of 1 + DEPTH items stay within the register budget (a third
-// item in flight measured no faster at m <= 2).
+// buffers of 1 + DEPTH items stay within the register budget (a third item
+// in flight measured no faster at m <= 2).  ITEM_DWORDS: a piece's decoded
+// size in dwords (the budget was measured with the pieces held decoded).
 template <int T, int M, int NR> struct Depth {
-    static constexpr int raw_dwords = (int)(sizeof(typename Tr<T>::Raw) / 4) * NR;
+    static constexpr int raw_dwords = Tr<T>::ITEM_DWORDS * NR;
     static constexpr int value = (raw_dwords * 3 + 2 * NR * M <= REX_DEPTH_BUDGET) ? 2 : 1;
 };
 
@@ -1170,7 +1248,11 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         // measured mixed, up to +4%); waves of one or two items take the
         // late half-workgroup issue below instead.
         constexpr bool XF = M <= REX_X_FIRST_MAX_M || (UNC && M >= REX_X_FIRST_UNC_MIN_M);
-        constexpr bool UP = UNC || XF;
+        // x by LDS DMA ahead of the first items' weights (types whose pieces
+        // take a fixed number of load instructions), chosen by the host where
+        // x exceeds what the register staging requests ahead (a.x_dma)
+        constexpr bool DMA = !NORM && !SUB && REX_X_DMA && Tr<T>::LOADS > 0 && M == 1;
+        constexpr bool UP = UNC || XF || DMA;
         auto prefetch_first = [&] {
             fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, A);
             if (DEPTH == 2) fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, B);
@@ -1186,10 +1268,17 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                                       (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);
             __syncthreads();
             if (late) prefetch_first();
+        } else if (DMA && a.x_dma) {
+            stage_x_dma<T, M>(xs, xb, a.xrs, a.k, XS, wave, nwaves, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            prefetch_first();
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_after_loads<DEPTH * NR * (DMA ? Tr<T>::LOADS : 0)>();
         } else if constexpr (XF) {
             // x is a few loads per thread, requested ahead of the weights, so
             // the barrier does not wait for every wave's weights
             stage_x_first<T, M>(xs, xb, a.xrs, a.k, XS, prefetch_first);
+            __syncthreads();
         } else {
             // From REX_LATE_HALF_MIN_M input rows on, the upper half of the
             // workgroup's waves request their first items only after the
@@ -1203,7 +1292,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             __syncthreads();
             if (late) prefetch_first();
         }
-        if constexpr (!NORM && XF) __syncthreads();
+
         if constexpr (kOffsets<T>) {
             stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, a.k);
             __syncthreads();
@@ -1263,6 +1352,12 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             }
             if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane, sc);
         }
+        // The walk leaves its last (unused) prefetch in flight; drain it
+        // here, where nothing follows, so that the compiler's wait
+        // bookkeeping does not carry it into the single-pass code (the two
+        // branches share a join block, and a load pending there forces a
+        // full wait ahead of the single pass' first weight loads).
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     }
 }
 
