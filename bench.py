@@ -589,6 +589,15 @@ def sweep(path, steps):
                         "frac_of_attainable_read": round(min(read_us) / us, 4),
                         "fp32_frac_of_published": round(fl / (us * 1e-6) / 1e12 / FP32_PUBLISHED_TFLOPS, 4),
                         "schedule": sch.asdict()})
+            if w.fused_norm:
+                # the same call as two launches on a work buffer, and the plain
+                # product on x alone (what the normalisation costs)
+                work = torch.empty(qfr.norm_work_bytes(k, m, batch), dtype=torch.uint8, device="cuda")
+                us2 = span_us(lambda i: qfr.row_exact_mv_add_rmsnorm_ws(t, Wd[i % copies], xd, rd, gd, 1e-5, hd, y, n,
+                                                                       k, m, batch, s, work=work))
+                us0 = span_us(lambda i: qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s))
+                res[-1].update({"one_kernel_us": round(us, 3), "two_launch_us": round(us2, 3),
+                                "plain_product_us": round(us0, 3)})
             print(json.dumps(res[-1]), file=sys.stderr, flush=True)
         del Wd
         torch.cuda.empty_cache()

@@ -189,7 +189,8 @@ int row_exact_mv_gather(row_exact_weight_t wt, const void *W, uint32_t num_exper
  * normalisation is linear per row, so the product runs on u = h * g (float32)
  * and each output is scaled once by the row's inverse RMS (float64, one
  * rounding); y keeps the row-exact contract (bitwise the same for m = 1 and
- * every row of m <= 8, for every packing).
+ * every row of m <= 8, for every packing).  One kernel: every workgroup
+ * forms the statistic of the rows it needs.
  *  x, r  : device float32, both in x's layout (strides as row_exact_mv).
  *  g     : device float32[k], or NULL for no weight (g = 1).
  *  eps   : finite, >= 0 (eps = 0 and an all-zero row give NaN outputs).
@@ -202,6 +203,33 @@ int row_exact_mv_gather(row_exact_weight_t wt, const void *W, uint32_t num_exper
 int row_exact_mv_add_rmsnorm(row_exact_weight_t wt, const void *W, const float *x, const float *r, const float *g,
                              float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                              const row_exact_strides_t *strides, hipStream_t stream);
+
+/* Bytes of the work buffer row_exact_mv_add_rmsnorm_ws needs: u (batch*m*k
+ * floats, rounded up to 256 bytes), then batch*m doubles. */
+#define ROW_EXACT_NORM_WORK_BYTES(k, m, batch)                                                                 \
+    ((((uint64_t)(batch) * (m) * (k) * 4u + 255u) & ~(uint64_t)255u) + (uint64_t)(batch) * (m) * 8u)
+
+/* row_exact_mv_add_rmsnorm as two launches on `stream`, with the same
+ * results bit for bit: the add and the statistic in a kernel of their own
+ * (writing h, u = h * g and each input row's inverse RMS into `work`), then
+ * the plain mat-vec on u, every output scaled by its row's value.  Faster
+ * from m = 4 on (the product keeps its staging of the input ahead of the
+ * weights, and the statistic is formed once instead of in every
+ * workgroup); one launch more.
+ *  work       : device buffer of at least ROW_EXACT_NORM_WORK_BYTES(k, m,
+ *               batch) bytes, 16-byte aligned, caller-owned, overwritten
+ *               (its contents are undefined afterwards); must not overlap W,
+ *               x, r, g, h or y, nor be in use by other work until the
+ *               stream has passed this call.
+ *  work_bytes : its size.
+ * Other arguments as row_exact_mv_add_rmsnorm.  Errors: as
+ * row_exact_mv_add_rmsnorm, plus ROW_EXACT_EARG (NULL work, work_bytes too
+ * small), ROW_EXACT_EALIGN and ROW_EXACT_EALIAS for work.  A launch error of
+ * the second kernel leaves h written and y untouched. */
+int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *x, const float *r, const float *g,
+                                float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                                const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
+                                hipStream_t stream);
 
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
  * depends on (wt, k) only; the packing fields may depend on every argument

@@ -19,6 +19,7 @@ __all__ = [
     "Weight", "Strides", "Schedule", "RowExactError", "LibraryMissing", "MAX_ROWS",
     "contiguous", "grouped_token_major", "library_path", "load_library",
     "row_exact_mv", "row_exact_mv_scheduled", "row_exact_mv_gather", "row_exact_mv_add_rmsnorm",
+    "row_exact_mv_add_rmsnorm_ws", "norm_work_bytes",
     "row_exact_schedule", "row_exact_row_bytes",
     "row_exact_required_bytes", "row_exact_dequant", "row_exact_last_error", "row_exact_launch_count",
     "row_exact_stream_read", "row_exact_stream_read_shapes",
@@ -117,6 +118,9 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_mv_gather.argtypes = [ctypes.c_int, P, u32, P, P, P, u32, u32, u32, u32, SP, P]
     lib.row_exact_mv_add_rmsnorm.restype = ctypes.c_int
     lib.row_exact_mv_add_rmsnorm.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32, SP, P]
+    lib.row_exact_mv_add_rmsnorm_ws.restype = ctypes.c_int
+    lib.row_exact_mv_add_rmsnorm_ws.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32, SP,
+                                                P, u64, P]
     lib.row_exact_schedule.restype = ctypes.c_int
     lib.row_exact_schedule.argtypes = [ctypes.c_int, u32, u32, u32, u32, SchP]
     lib.row_exact_row_bytes.restype = u64
@@ -236,11 +240,8 @@ def row_exact_mv_gather(wt: int, W: Any, num_experts: int, expert_ids: Any, x: A
     _check(lib.row_exact_mv_gather(int(wt), wp, num_experts, ip, xp, yp, n, k, m, batch, sp, _stream_handle(stream)))
 
 
-def row_exact_mv_add_rmsnorm(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int, k: int,
-                             m: int, batch: int = 1, strides: Optional[Strides] = None, stream: Any = None) -> None:
-    """Enqueue ``h = x + r``, ``x' = h / sqrt(mean(h^2) + eps) * g``,
-    ``y = W . x'`` per input row (see ``row_exact_mv_add_rmsnorm``); ``g`` and
-    ``h`` may be None."""
+def _norm_call(entry: str, wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int, k: int,
+               m: int, batch: int, strides: Optional[Strides], stream: Any, extra: tuple = ()) -> None:
     wt = Weight(wt)
     lib = load_library()
     _dtype_check(wt, W, x, y)
@@ -254,10 +255,45 @@ def row_exact_mv_add_rmsnorm(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float
             raise ValueError(f"{name} holds {have} bytes, needs {need}")
     ptr = lambda t, name: None if t is None else _ptr_and_bytes(t, name)[0]
     sp = ctypes.byref(strides) if strides is not None else None
-    _check(lib.row_exact_mv_add_rmsnorm(int(wt), ptr(W, "weight"), ptr(x, "input"), ptr(r, "r"), ptr(g, "g"),
-                                        float(eps), ptr(h, "h"), ptr(y, "output"), n, k, m, batch, sp,
-                                        _stream_handle(stream)))
+    _check(getattr(lib, entry)(int(wt), ptr(W, "weight"), ptr(x, "input"), ptr(r, "r"), ptr(g, "g"), float(eps),
+                               ptr(h, "h"), ptr(y, "output"), n, k, m, batch, sp, *extra, _stream_handle(stream)))
 
+
+def row_exact_mv_add_rmsnorm(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int, k: int,
+                             m: int, batch: int = 1, strides: Optional[Strides] = None, stream: Any = None) -> None:
+    """Enqueue ``h = x + r``, ``x' = h / sqrt(mean(h^2) + eps) * g``,
+    ``y = W . x'`` per input row (see ``row_exact_mv_add_rmsnorm``); ``g`` and
+    ``h`` may be None."""
+    _norm_call("row_exact_mv_add_rmsnorm", wt, W, x, r, g, eps, h, y, n, k, m, batch, strides, stream)
+
+
+def norm_work_bytes(k: int, m: int, batch: int = 1) -> int:
+    """Bytes of the work buffer of :func:`row_exact_mv_add_rmsnorm_ws`
+    (ROW_EXACT_NORM_WORK_BYTES)."""
+    return ((batch * m * k * 4 + 255) & ~255) + batch * m * 8
+
+
+def row_exact_mv_add_rmsnorm_ws(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int, k: int,
+                                m: int, batch: int = 1, strides: Optional[Strides] = None, work: Any = None,
+                                stream: Any = None) -> None:
+    """:func:`row_exact_mv_add_rmsnorm` as two launches on a work buffer
+    (same bits; see ``row_exact_mv_add_rmsnorm_ws``).  ``work``: a GPU tensor
+    or device pointer of at least :func:`norm_work_bytes` bytes; None takes
+    one from torch's caching allocator on the call's stream."""
+    need = norm_work_bytes(k, m, batch)
+    if work is None:
+        # torch's caching allocator reuses a block only after the stream it was
+        # taken on has passed its last use, so the buffer is taken on the
+        # call's own stream (a raw handle cannot be given to torch)
+        if isinstance(stream, int):
+            raise ValueError("pass work explicitly when the stream is a raw handle")
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            work = torch.empty(need, dtype=torch.uint8, device=s.device)
+    wp, wlen = _ptr_and_bytes(work, "work")
+    _norm_call("row_exact_mv_add_rmsnorm_ws", wt, W, x, r, g, eps, h, y, n, k, m, batch, strides, stream,
+               (wp, need if wlen is None else wlen))
 
 def row_exact_schedule(wt: int, n: int, k: int, m: int, batch: int = 1) -> Schedule:
     """Default schedule for a shape on the current device."""

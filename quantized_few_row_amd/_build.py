@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librow_exact_mv.so")
 ARCH = os.environ.get("ROW_EXACT_ARCH", "gfx950")
 
-SOURCES = ["re_api.hip", "re_probe.hip", "re_mv_f16.hip", "re_mv_q8_0.hip", "re_mv_q4_k.hip", "re_mv_q6_k.hip", "re_mv_q5_0.hip", "re_mv_f32.hip", "re_mv_bf16.hip"]
+SOURCES = ["re_api.hip", "re_probe.hip", "re_norm.hip", "re_mv_f16.hip", "re_mv_q8_0.hip", "re_mv_q4_k.hip", "re_mv_q6_k.hip", "re_mv_q5_0.hip", "re_mv_f32.hip", "re_mv_bf16.hip"]
 HEADERS = ["re_internal.h", "re_kernels.h"]
 
 

@@ -528,9 +528,16 @@ int validate_norm(const Norm &nm, const void *W, const float *x, const float *y,
     return 0;
 }
 
+int run_norm_two_launch(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m,
+                        uint32_t batch, const row_exact_strides_t &s, const Norm &nm, hipStream_t stream,
+                        void *work);
+
+// row_scale: per (batch entry, input row) output scales, [batch][m] (the
+// second launch of the two-launch fused normalisation), or NULL.
 int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
         const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream,
-        const int32_t *ids = nullptr, uint32_t num_experts = 0, const Norm *norm = nullptr) {
+        const int32_t *ids = nullptr, uint32_t num_experts = 0, const Norm *norm = nullptr,
+        const double *row_scale = nullptr, void *norm_work = nullptr) {
     g_err.clear();
     const row_exact_strides_t s = resolve_strides(strides, m, n, k);
     uint64_t wb, xbytes, ybytes;
@@ -539,6 +546,7 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     if (norm) {
         rc = validate_norm(*norm, W, x, y, k, wb, xbytes, ybytes);
         if (rc) return rc;
+        if (norm_work) return run_norm_two_launch(t, W, x, y, n, k, m, batch, s, *norm, stream, norm_work);
     }
     if (pin) {
         rc = check_schedule_fields(t, k, *pin);
@@ -610,6 +618,8 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
         const bool dma_type = t == kQ6K;  // the types with a DMA staging path (Tr<T>::LOADS > 0)
         a.x_dma = (a.nchunks == 1 && m == 1 && !norm && dma_type && k > ahead) ? 1u : 0u;
     }
+    a.row_scale = row_scale;
+    a.row_scale_stride = m;
     {
         // items a wave walks in the single pass: its row groups x wave steps
         const uint32_t waves = sch.waves_per_workgroup;
@@ -626,6 +636,53 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     g_launches.fetch_add(1, std::memory_order_relaxed);
     return 0;
+}
+
+// Bytes of the two-launch fused normalisation's work buffer: u ([batch][m][k]
+// floats, rounded up to 256 bytes) then the inverse RMS values ([batch][m]
+// doubles); ROW_EXACT_NORM_WORK_BYTES in the header.
+uint64_t norm_work_bytes(uint32_t k, uint32_t m, uint32_t batch) {
+    const uint64_t u = ((uint64_t)batch * m * k * sizeof(float) + 255) & ~255ull;
+    return u + (uint64_t)batch * m * sizeof(double);
+}
+
+// The fused add + RMS norm as two launches on `stream`: norm_rows_kernel
+// writes h (when requested), u = (x + r) * g and each input row's inverse
+// RMS into the work buffer (norm_work_bytes, a device address); the plain
+// mat-vec multiplies u and scales each output by its row's value.  Outputs
+// have the bits of the single-kernel form (same u, same statistic order,
+// same scaling).  Arguments are validated by the caller.
+int run_norm_two_launch(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m,
+                        uint32_t batch, const row_exact_strides_t &s, const Norm &nm, hipStream_t stream,
+                        void *work) {
+    float *u = (float *)work;
+    double *inv = (double *)((uint8_t *)work + (((uint64_t)batch * m * k * sizeof(float) + 255) & ~255ull));
+    NormArgs na;
+    na.x = x;
+    na.r = nm.r;
+    na.g = nm.g;
+    na.h = nm.h;
+    na.u = u;
+    na.inv = inv;
+    na.xbs = s.x_batch_stride;
+    na.xrs = s.x_row_stride;
+    na.k = k;
+    na.m = m;
+    na.eps = nm.eps;
+    int rc = 0;
+    hipError_t e = launch_norm_rows(na, batch, stream);
+    if (e != hipSuccess) {
+        rc = fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    } else {
+        g_launches.fetch_add(1, std::memory_order_relaxed);
+        row_exact_strides_t su;
+        su.x_row_stride = k;
+        su.x_batch_stride = m * k;
+        su.y_row_stride = s.y_row_stride;
+        su.y_batch_stride = s.y_batch_stride;
+        rc = run(t, W, u, y, n, k, m, batch, &su, nullptr, stream, nullptr, 0, nullptr, inv);
+    }
+    return rc;
 }
 
 }  // namespace
@@ -662,6 +719,33 @@ int row_exact_mv_add_rmsnorm(row_exact_weight_t wt, const void *W, const float *
                              const row_exact_strides_t *strides, hipStream_t stream) {
     const Norm nm{r, g, h, eps};
     return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm);
+}
+
+int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *x, const float *r, const float *g,
+                                float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                                const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
+                                hipStream_t stream) {
+    g_err.clear();
+    int rc = check_shape((int)wt, n, k, m, batch);
+    if (rc) return rc;
+    if (!work) return fail(ROW_EXACT_EARG, "work must be a non-NULL device pointer");
+    if ((uintptr_t)work % 16) return fail(ROW_EXACT_EALIGN, "work must sit on a 16-byte boundary");
+    const uint64_t need = norm_work_bytes(k, m, batch);
+    if (work_bytes < need)
+        return fail(ROW_EXACT_EARG, "work holds %llu bytes, the call needs %llu", (unsigned long long)work_bytes,
+                    (unsigned long long)need);
+    // work is written: it must not overlap any operand
+    const row_exact_strides_t s = resolve_strides(strides, m, n, k);
+    uint64_t wb = 0, xb = 0, yb = 0;
+    rc = sizes((int)wt, n, k, m, batch, s, wb, xb, yb);
+    if (rc) return rc;
+    const uintptr_t wp = (uintptr_t)work;
+    if (overlap(wp, need, (uintptr_t)W, wb) || overlap(wp, need, (uintptr_t)x, xb) ||
+        overlap(wp, need, (uintptr_t)r, xb) || overlap(wp, need, (uintptr_t)y, yb) ||
+        (h && overlap(wp, need, (uintptr_t)h, xb)) || (g && overlap(wp, need, (uintptr_t)g, 4ull * k)))
+        return fail(ROW_EXACT_EALIAS, "work overlaps W, x, r, g, h or y");
+    const Norm nm{r, g, h, eps};
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, nullptr, work);
 }
 
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,

@@ -48,7 +48,25 @@ struct MvArgs {
     // weights (single pass, m = 1, x larger than the register staging
     // requests ahead of them)
     uint32_t x_dma;
+    // Each output (b, j, i) scaled by row_scale[b * row_scale_stride + j]
+    // (float64, one rounding), or NULL: the product of the two-launch fused
+    // add + RMS norm runs on u = (x + r) * g with the rows' inverse RMS here.
+    const double *row_scale;
+    uint32_t row_scale_stride;
 };
+
+// The add + RMS statistics of the fused normalisation (norm_rows_kernel):
+// one workgroup of 256 threads per (batch entry, input row).
+struct NormArgs {
+    const float *x, *r, *g;  // x and r in the product's x layout; g: k weights or NULL
+    float *h;                // x + r in the same layout, or NULL
+    float *u;                // (x + r) * g, contiguous [batch][m][k]
+    double *inv;             // inverse RMS per (batch entry, input row), [batch][m]
+    uint64_t xbs;
+    uint32_t xrs, k, m;
+    float eps;
+};
+hipError_t launch_norm_rows(const NormArgs &a, uint32_t batch, hipStream_t s);
 
 struct DqArgs {
     const uint8_t *W;

@@ -498,16 +498,25 @@ __device__ __forceinline__ typename Tr<T>::Raw load_walk(const uint8_t *R, uint3
         return Tr<T>::load(R, o0, p, k);
 }
 
-// Per-row output scale of the fused normalisation (part == NULL: none).
+// Per-row output scale of the fused normalisation: either the four
+// float64 group sums of each input row's statistic in LDS (part, the
+// single-kernel form), or each row's inverse RMS formed from the same sums
+// by norm_rows_kernel (inv, one double per input row of the batch entry).
+// Both give (float)((double)v * inv) with the same inv; neither: v.
 struct RowScale {
     const double *part;
+    const double *inv;
     uint32_t k;
     float eps;
     __device__ __forceinline__ float apply(float v, uint32_t j) const {
+        if (inv) return (float)((double)v * inv[j]);
         if (!part) return v;
-        const double s = (part[4 * j] + part[4 * j + 1]) + (part[4 * j + 2] + part[4 * j + 3]);
-        const double inv = 1.0 / __builtin_sqrt(s / (double)k + (double)eps);
-        return (float)((double)v * inv);
+        return (float)((double)v * inv_rms(part + 4 * j, k, eps));
+    }
+    // 1 / sqrt(mean + eps) from the four group sums, added as (s0 + s1) + (s2 + s3).
+    static __device__ __forceinline__ double inv_rms(const double *p4, uint32_t k, float eps) {
+        const double s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+        return 1.0 / __builtin_sqrt(s / (double)k + (double)eps);
     }
 };
 
@@ -1235,7 +1244,8 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         const uint32_t gfirst = lg;
         Raw A[NR], B[NR], C[NR];
         double *part = (double *)((uint8_t *)xs + a.norm_offset);
-        const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
+        const RowScale sc{NORM ? part : nullptr, a.row_scale ? a.row_scale + (uint64_t)b * a.row_scale_stride : nullptr,
+                          a.k, a.eps};
         // The first DEPTH items' loads: straight-line (see fetch_item) for
         // the unconditional walk and for x staged ahead of them (so that the
         // x loads can be waited for without them); under a branch otherwise
@@ -1318,7 +1328,8 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         // 64 lanes per row): every wave of the workgroup works on one row
         // group per round and all waves stage each pass together.
         double *part = (double *)((uint8_t *)xs + a.norm_offset);
-        const RowScale sc{NORM ? part : nullptr, a.k, a.eps};
+        const RowScale sc{NORM ? part : nullptr, a.row_scale ? a.row_scale + (uint64_t)b * a.row_scale_stride : nullptr,
+                          a.k, a.eps};
         const float *rb = NORM ? a.r + b * a.xbs : nullptr;
         if constexpr (NORM)  // the pass loop's first barrier orders these writes before any store
             norm_partials<T, M, false>(part, nullptr, XS, xb, rb, a.g, (a.h && w == 0) ? a.h + b * a.xbs : nullptr,

@@ -36,7 +36,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = qfr.load_library()
     declared = _declared_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 13, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -322,3 +322,41 @@ def test_add_rmsnorm_invalid_arguments(kw, code, text):
     assert rc == code, (rc, msg)
     assert text in msg, msg
     assert qfr.row_exact_launch_count() == before
+
+
+WK = 0x7F6000000000
+
+
+def _norm_ws(work=WK, work_bytes=1 << 20, **kw):
+    lib = qfr.load_library()
+    a = dict(r=RP, g=GP, h=HP, eps=1e-5, x=XP, y=YP, W=WP, n=64, k=256, m=4, wt=Weight.Q8_0)
+    a.update(kw)
+    rc = lib.row_exact_mv_add_rmsnorm_ws(int(a["wt"]), a["W"], a["x"], a["r"], a["g"], a["eps"], a["h"], a["y"], a["n"],
+                                         a["k"], a["m"], 1, None, work, work_bytes, None)
+    return rc, qfr.row_exact_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(work=0), -1, "work must be"),
+    (dict(work=WK + 8), -2, "work must sit on a 16-byte boundary"),
+    (dict(work_bytes=4 * 256 * 4), -1, "the call needs"),
+    (dict(work=YP), -4, "work overlaps"),
+    (dict(work=XP + 16), -4, "work overlaps"),
+    (dict(work=HP), -4, "work overlaps"),
+    (dict(work=GP), -4, "work overlaps"),
+    (dict(m=9), -1, "m = 9"),
+    (dict(r=0), -1, "r must be"),
+])
+def test_add_rmsnorm_ws_invalid_arguments(kw, code, text):
+    before = qfr.row_exact_launch_count()
+    rc, msg = _norm_ws(**kw)
+    assert rc == code, (rc, msg)
+    assert text in msg, msg
+    assert qfr.row_exact_launch_count() == before
+
+
+def test_norm_work_bytes_is_the_header_formula():
+    # u (batch*m*k floats) rounded up to 256 bytes, then batch*m doubles
+    assert qfr.norm_work_bytes(256, 4, 1) == 4096 + 32
+    assert qfr.norm_work_bytes(4, 1, 1) == 256 + 8
+    assert qfr.norm_work_bytes(4096, 8, 16) == 16 * 8 * 4096 * 4 + 16 * 8 * 8

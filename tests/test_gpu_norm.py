@@ -135,3 +135,60 @@ def test_add_rmsnorm_full_workgroups(t, n, k):
         yb = bits(y).reshape(m, n)
         for j in range(m):
             assert np.array_equal(yb[j], y1[j]), f"m={m} row {j} differs from its m = 1 run"
+
+
+def _run_ws(t, Wd, xd, rd, gd, eps, n, k, m, batch=1, strides=None, fill=float("nan")):
+    _, xb, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, strides)
+    y = torch.full((yb // 4,), fill, device="cuda:0")
+    h = torch.full((xb // 4,), fill, device="cuda:0")
+    # a work buffer full of garbage: the call writes everything it reads
+    work = torch.full((qfr.norm_work_bytes(k, m, batch) // 4 + 4,), float("nan"), device="cuda:0")
+    qfr.row_exact_mv_add_rmsnorm_ws(t, Wd, xd, rd, gd, eps, h, y, n, k, m, batch, strides, work=work)
+    torch.cuda.synchronize()
+    return h, y
+
+
+@pytest.mark.parametrize("t", TYPES, ids=IDS)
+@pytest.mark.parametrize("with_g", [True, False])
+def test_add_rmsnorm_two_launch_matches_one_kernel(t, with_g):
+    """row_exact_mv_add_rmsnorm_ws (statistic in a kernel of its own, then the
+    plain product on u) gives every output and h the bits of the one-kernel
+    call, at every m."""
+    n, k = SHAPES[t]
+    W = wl.weights(t, n, k, seed=1600 + t)
+    x = wl.activations(8, k, seed=1601 + t)
+    r = wl.activations(8, k, seed=1602 + t)
+    g = (1.0 + 0.1 * wl.activations(1, k, seed=1603 + t)[0]).astype(np.float32) if with_g else None
+    Wd, xd, rd = to_dev(W.ravel()), to_dev(x.ravel()), to_dev(r.ravel())
+    gd = to_dev(g) if with_g else None
+    for m in range(1, 9):
+        h1, y1 = _run(t, Wd, xd, rd, gd, 1e-5, n, k, m)
+        h2, y2 = _run_ws(t, Wd, xd, rd, gd, 1e-5, n, k, m)
+        assert np.array_equal(bits(y1), bits(y2)), f"m={m}: y differs between the two forms"
+        assert np.array_equal(bits(h1), bits(h2)), f"m={m}: h differs between the two forms"
+
+
+def test_add_rmsnorm_two_launch_batched_and_multipass():
+    """Batch-major strided views with gaps (nothing outside them written) and
+    a k that needs several LDS passes at m = 8: the two forms agree bitwise."""
+    t = wl.Q6_K
+    for n, k, m, batch, s in ((29, 4352, 4, 3, Strides(4352 + 8, 5 * (4352 + 8), 29 + 3, 5 * (29 + 3))),
+                              (9, 14336, 8, 1, None)):
+        W = wl.weights(t, n * batch, k, seed=1700 + k)
+        _, xb, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, s)
+        x = wl.activations(1, xb // 4, seed=1701)[0]
+        r = wl.activations(1, xb // 4, seed=1702)[0]
+        g = (1.0 + 0.1 * wl.activations(1, k, seed=1703)[0]).astype(np.float32)
+        Wd, xd, rd, gd = to_dev(W.ravel()), to_dev(x), to_dev(r), to_dev(g)
+        h1, y1 = _run(t, Wd, xd, rd, gd, 1e-6, n, k, m, batch, s)
+        h2, y2 = _run_ws(t, Wd, xd, rd, gd, 1e-6, n, k, m, batch, s)
+        assert np.array_equal(bits(y1), bits(y2)), f"k={k}: y"
+        assert np.array_equal(bits(h1), bits(h2)), f"k={k}: h"
+        if s is not None:
+            yc = y2.cpu().numpy()
+            ymask = np.zeros(yc.size, bool)
+            for b in range(batch):
+                for j in range(m):
+                    o = b * s.y_batch_stride + j * s.y_row_stride
+                    ymask[o:o + n] = True
+            assert np.all(np.isnan(yc[~ymask])), "y written outside its view"
