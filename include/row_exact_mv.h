@@ -231,6 +231,30 @@ int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const floa
                                 const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
                                 hipStream_t stream);
 
+/* Bytes of the scratch array behind row_exact_mv_add_rmsnorm_noalloc, per
+ * GPU: it serves calls whose ROW_EXACT_NORM_WORK_BYTES(k, m, batch) is at
+ * most this. */
+#define ROW_EXACT_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* row_exact_mv_add_rmsnorm_ws for callers that cannot allocate device
+ * memory, not even a work buffer (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same two kernels and
+ * the same results bit for bit, the work buffer being an array of
+ * ROW_EXACT_NOALLOC_SCRATCH_BYTES per GPU that the library holds from its
+ * first call on that GPU until the process ends.  Allocates nothing.  Every
+ * call on a GPU uses that GPU's one array: calls that overlap on one GPU
+ * (other streams, other host threads) race and give undefined results;
+ * calls in order on one stream are safe.  The array keeps the last call's
+ * contents; nothing in it needs clearing (each call writes all it reads).
+ * Arguments as row_exact_mv_add_rmsnorm.  Errors: as
+ * row_exact_mv_add_rmsnorm, plus ROW_EXACT_EEXTENT when
+ * ROW_EXACT_NORM_WORK_BYTES(k, m, batch) exceeds the array, ROW_EXACT_EHIP
+ * when the array's device address cannot be had. */
+int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const float *x, const float *r,
+                                     const float *g, float eps, float *h, float *y, uint32_t n, uint32_t k,
+                                     uint32_t m, uint32_t batch, const row_exact_strides_t *strides,
+                                     hipStream_t stream);
+
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
  * depends on (wt, k) only; the packing fields may depend on every argument
  * and on the current device.  Unlike the page's query (weight, rows, k), this

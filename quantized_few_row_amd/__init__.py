@@ -19,7 +19,7 @@ __all__ = [
     "Weight", "Strides", "Schedule", "RowExactError", "LibraryMissing", "MAX_ROWS",
     "contiguous", "grouped_token_major", "library_path", "load_library",
     "row_exact_mv", "row_exact_mv_scheduled", "row_exact_mv_gather", "row_exact_mv_add_rmsnorm",
-    "row_exact_mv_add_rmsnorm_ws", "norm_work_bytes",
+    "row_exact_mv_add_rmsnorm_ws", "norm_work_bytes", "row_exact_mv_add_rmsnorm_noalloc", "NOALLOC_SCRATCH_BYTES",
     "row_exact_schedule", "row_exact_row_bytes",
     "row_exact_required_bytes", "row_exact_dequant", "row_exact_last_error", "row_exact_launch_count",
     "row_exact_stream_read", "row_exact_stream_read_shapes",
@@ -29,6 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librow_exact_mv.so")
 
 MAX_ROWS = 8
+NOALLOC_SCRATCH_BYTES = 4 << 20  # ROW_EXACT_NOALLOC_SCRATCH_BYTES
 
 ERRORS = {-1: "EARG", -2: "EALIGN", -3: "ESTRIDE", -4: "EALIAS", -5: "EEXTENT", -6: "ESCHEDULE", -7: "EHIP"}
 
@@ -118,6 +119,9 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_mv_gather.argtypes = [ctypes.c_int, P, u32, P, P, P, u32, u32, u32, u32, SP, P]
     lib.row_exact_mv_add_rmsnorm.restype = ctypes.c_int
     lib.row_exact_mv_add_rmsnorm.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32, SP, P]
+    lib.row_exact_mv_add_rmsnorm_noalloc.restype = ctypes.c_int
+    lib.row_exact_mv_add_rmsnorm_noalloc.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32,
+                                                     SP, P]
     lib.row_exact_mv_add_rmsnorm_ws.restype = ctypes.c_int
     lib.row_exact_mv_add_rmsnorm_ws.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32, SP,
                                                 P, u64, P]
@@ -294,6 +298,14 @@ def row_exact_mv_add_rmsnorm_ws(wt: int, W: Any, x: Any, r: Any, g: Any, eps: fl
     wp, wlen = _ptr_and_bytes(work, "work")
     _norm_call("row_exact_mv_add_rmsnorm_ws", wt, W, x, r, g, eps, h, y, n, k, m, batch, strides, stream,
                (wp, need if wlen is None else wlen))
+
+def row_exact_mv_add_rmsnorm_noalloc(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int,
+                                     k: int, m: int, batch: int = 1, strides: Optional[Strides] = None,
+                                     stream: Any = None) -> None:
+    """:func:`row_exact_mv_add_rmsnorm_ws` without any allocation (the
+    library's fixed scratch array; see ``row_exact_mv_add_rmsnorm_noalloc``)."""
+    _norm_call("row_exact_mv_add_rmsnorm_noalloc", wt, W, x, r, g, eps, h, y, n, k, m, batch, strides, stream)
+
 
 def row_exact_schedule(wt: int, n: int, k: int, m: int, batch: int = 1) -> Schedule:
     """Default schedule for a shape on the current device."""

@@ -646,6 +646,34 @@ uint64_t norm_work_bytes(uint32_t k, uint32_t m, uint32_t batch) {
     return u + (uint64_t)batch * m * sizeof(double);
 }
 
+// Scratch of row_exact_mv_add_rmsnorm_noalloc (the work buffer of the
+// two-launch fused normalisation, for callers that cannot allocate): one
+// array per GPU, held until the process ends.  Host code never
+// uses its name as an address (that is a host-side stand-in); it asks the
+// runtime for the array's device address once per device.
+static __device__ __align__(256) uint8_t scratch[ROW_EXACT_NOALLOC_SCRATCH_BYTES];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with it current).
+int noalloc_scratch(void *&out) {
+    static std::mutex mu;
+    static void *ptrs[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(ROW_EXACT_EHIP, "device %d beyond the library's 64-device table", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(ROW_EXACT_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        ptrs[dev] = p;
+    }
+    out = ptrs[dev];
+    return 0;
+}
+
 // The fused add + RMS norm as two launches on `stream`: norm_rows_kernel
 // writes h (when requested), u = (x + r) * g and each input row's inverse
 // RMS into the work buffer (norm_work_bytes, a device address); the plain
@@ -746,6 +774,25 @@ int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const floa
         return fail(ROW_EXACT_EALIAS, "work overlaps W, x, r, g, h or y");
     const Norm nm{r, g, h, eps};
     return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, nullptr, work);
+}
+
+int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const float *x, const float *r,
+                                     const float *g, float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m,
+                                     uint32_t batch, const row_exact_strides_t *strides, hipStream_t stream) {
+    g_err.clear();
+    int rc = check_shape((int)wt, n, k, m, batch);
+    if (rc) return rc;
+    const uint64_t need = norm_work_bytes(k, m, batch);
+    if (need > ROW_EXACT_NOALLOC_SCRATCH_BYTES)
+        return fail(ROW_EXACT_EEXTENT,
+                    "the call needs %llu bytes of scratch (ROW_EXACT_NORM_WORK_BYTES), the allocation-free "
+                    "scratch holds %u",
+                    (unsigned long long)need, (unsigned)ROW_EXACT_NOALLOC_SCRATCH_BYTES);
+    void *ptr = nullptr;
+    rc = noalloc_scratch(ptr);
+    if (rc) return rc;
+    const Norm nm{r, g, h, eps};
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, nullptr, ptr);
 }
 
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,

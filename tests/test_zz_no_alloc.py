@@ -1,6 +1,7 @@
 """The allocation-free fused add + RMS norm (row_exact_mv_add_rmsnorm_noalloc)
-called through the C ABI: its outputs (y and h) are bitwise those of
-row_exact_mv_add_rmsnorm on the same inputs, for two calls in a row (the
+called through the C ABI: its outputs (y and h) are bitwise those of the
+entry point it is a variant of, row_exact_mv_add_rmsnorm_ws (same kernels on
+a caller work buffer), on the same inputs, for two calls in a row (the
 second smaller, so the fixed scratch array holds the first call's contents
 when the second starts), and a call that needs more scratch than the array
 holds is refused without touching y."""
@@ -30,8 +31,12 @@ def _call(entry, t, Wd, xd, rd, gd, n, k, m):
     y = torch.full((m * n,), float("nan"), device="cuda:0")
     h = torch.full((m * k,), float("nan"), device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
+    extra = ()
+    if entry.endswith("_ws"):
+        work = torch.full((qfr.norm_work_bytes(k, m) // 4,), float("nan"), device="cuda:0")
+        extra = (work.data_ptr(), work.numel() * 4)
     rc = getattr(lib, entry)(int(t), Wd.data_ptr(), xd.data_ptr(), rd.data_ptr(), gd.data_ptr(), ctypes.c_float(1e-5),
-                             h.data_ptr(), y.data_ptr(), n, k, m, 1, None, stream)
+                             h.data_ptr(), y.data_ptr(), n, k, m, 1, None, *extra, stream)
     assert rc == 0, (rc, qfr.row_exact_last_error())
     torch.cuda.synchronize()
     return y, h
@@ -43,7 +48,7 @@ def test_noalloc_matches_the_allocating_entry_point_twice():
         print(f"[noalloc] type {wl.TYPE_NAMES[t]} n={n} k={k} m={m}", flush=True)
         Wd, xd, rd, gd = _inputs(t, n, k, m, seed)
         y_na, h_na = _call("row_exact_mv_add_rmsnorm_noalloc", t, Wd, xd, rd, gd, n, k, m)
-        y_ref, h_ref = _call("row_exact_mv_add_rmsnorm", t, Wd, xd, rd, gd, n, k, m)
+        y_ref, h_ref = _call("row_exact_mv_add_rmsnorm_ws", t, Wd, xd, rd, gd, n, k, m)
         assert torch.equal(y_na.view(torch.int32), y_ref.view(torch.int32)), "y differs"
         assert torch.equal(h_na.view(torch.int32), h_ref.view(torch.int32)), "h differs"
         assert not torch.isnan(y_na).any()
