@@ -18,7 +18,8 @@
  * m = 1 or as one row of any m <= 8, and identical across repeated calls.  The
  * only thing that changes the bits of an output is the reduction split
  * (row_exact_schedule_t.k_split), which the library derives from the weight
- * type and k alone; every other schedule field only packs work.
+ * type, k and the rows n of one batch entry (never from m or the batch);
+ * every other schedule field only packs work.
  *
  * Conventions for every entry point:
  *  - Pointers W, x, y, out are device pointers (HBM).  The caller owns them;
@@ -89,11 +90,22 @@ typedef struct {
 } row_exact_strides_t;
 
 /* Launch schedule (RowExactMatvecSchedule, re-planned for CDNA4 wave64).
- *  k_split              : numerics.  Waves whose partial sums form one output
- *                         (1: the 64 lanes of one wave split K and a fixed
- *                         DPP/permlane tree reduces them).  Derived from
- *                         (weight type, k) by row_exact_schedule(); a pinned
- *                         schedule must carry the same value.
+ *  k_split              : numerics.  Waves whose partial sums form one output:
+ *                         1, 2, 4 or 8.  With 1 the 64 lanes of one wave
+ *                         split the row and a fixed permlane/DPP tree adds
+ *                         them; with K > 1 wave s of K takes the row's wave
+ *                         steps s, s + K, s + 2K, ..., each wave's lanes are
+ *                         added by the same tree, and the K wave sums by the
+ *                         pairwise tree ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))
+ *                         cut to K terms.  row_exact_schedule() derives it
+ *                         from (weight type, k, n): the largest power of two
+ *                         <= min(1024 / n, 8, whole 64-piece wave steps of
+ *                         a row); 1 for rows of at most 32 pieces or fewer
+ *                         than 3 whole wave steps.  A pinned
+ *                         schedule may carry any valid value (<= the row's
+ *                         wave steps, dividing waves_per_workgroup); outputs
+ *                         then follow that value, e.g. to keep the bits of
+ *                         an unsharded product on a row shard.
  *  rows_per_wave        : packing.  Weight rows a wave streams together,
  *                         sharing each input load: 1, 2 or 4.
  *  waves_per_workgroup  : packing.  1..8 (64..512 threads).
@@ -105,7 +117,8 @@ typedef struct {
  *                         pass; >= k means one pass.  Otherwise a multiple of
  *                         the weight type's wave step (512 values for F16 /
  *                         BF16, 256 for F32, 2048 for Q8_0 / Q5_0, 4096 for
- *                         Q4_K / Q6_K).
+ *                         Q4_K / Q6_K); with k_split > 1 a pass of fewer than
+ *                         k_split wave steps leaves some waves idle.
  * Packing fields never change the bits of y. */
 typedef struct {
     uint32_t k_split;
@@ -147,9 +160,11 @@ int row_exact_mv(row_exact_weight_t wt, const void *W, const float *x, float *y,
 
 /* As row_exact_mv with an explicit schedule
  * (dispatch_row_exact_matvec_scheduled).  Outputs are bitwise identical to
- * row_exact_mv's for every valid schedule: packing is inert and k_split must
- * equal the derived value.  Extra error: ROW_EXACT_ESCHEDULE (a field out of
- * range, k_chunk not a wave-step multiple, LDS need above the device limit). */
+ * row_exact_mv's for every valid schedule with the derived k_split: packing
+ * is inert; another k_split gives that split's sums.  Extra error:
+ * ROW_EXACT_ESCHEDULE (a field out of range, k_split not dividing the waves
+ * or above the row's wave steps, k_chunk not a wave-step multiple, LDS need
+ * above the device limit). */
 int row_exact_mv_scheduled(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n,
                            uint32_t k, uint32_t m, uint32_t batch, const row_exact_strides_t *strides,
                            const row_exact_schedule_t *schedule, hipStream_t stream);
@@ -256,7 +271,7 @@ int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const
                                      hipStream_t stream);
 
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
- * depends on (wt, k) only; the packing fields may depend on every argument
+ * depends on (wt, k, n) only; the packing fields may depend on every argument
  * and on the current device.  Unlike the page's query (weight, rows, k), this
  * one takes m: the packing is chosen per m because the m-row kernel's
  * register and LDS needs decide how many rows a wave and how many workgroups

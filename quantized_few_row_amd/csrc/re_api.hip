@@ -139,8 +139,12 @@ uint32_t sx_stride(int t, uint32_t k, uint32_t k_chunk) {
 size_t lds_sx_offset(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
     return lds_x_bytes(t, m, k, k_chunk) + (size_t)4 * m * sizeof(double);
 }
-size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
-    return lds_sx_offset(t, m, k, k_chunk) + (size_t)m * sx_stride(t, k, k_chunk) * sizeof(float);
+// Then, for a K split, 32 float partial sums per wave (8 waves).
+size_t lds_kp_offset(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
+    return (lds_sx_offset(t, m, k, k_chunk) + (size_t)m * sx_stride(t, k, k_chunk) * sizeof(float) + 15) & ~(size_t)15;
+}
+size_t lds_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk, uint32_t k_split = 1) {
+    return lds_kp_offset(t, m, k, k_chunk) + (k_split > 1 ? 8 * 32 * sizeof(float) : 0);
 }
 
 typedef unsigned __int128 u128;
@@ -248,9 +252,30 @@ int validate_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint
     return 0;
 }
 
-// Reduction split: a function of (type, k) only.  Every output is the
-// 64-lane tree sum of one wave's lane chains.
-uint32_t derived_k_split(int, uint32_t) { return 1; }
+// Reduction split (numerics): the waves whose partial sums form one output,
+// 1, 2, 4 or 8, derived from the weight shape alone -- type, k and the rows
+// n of one batch entry -- never from m, the batch or the packing (the page
+// derives its simdgroup split from (weight, rows, k) the same way; leaving
+// the batch out keeps a batched or gathered call bitwise equal to separate
+// calls per entry).  Skinny outputs deal each row's wave steps over K
+// waves, so that rows times K reach about one wave per SIMD of a 256-CU
+// device (1024; a constant, so that the bits do not depend on the device),
+// without a wave holding less than one whole wave step: K is the largest
+// power of two <= min(1024 / n, 8, whole wave steps of a row).  Rows of at
+// most 32 pieces (16 or 32 lanes per row) and rows of fewer than 3 whole
+// wave steps are not split: at 2 steps the split measured slower at m <= 4
+// (Q8_0 512 x 4096, m = 1: 3.2 us unsplit, 3.7 us split in 2), the one
+// wave's single-pass walk being cheaper than the partial-sum exchange.  At
+// n >= 1024, K is 1: one wave's 64 lanes per output.
+uint32_t derived_k_split(int t, uint32_t k, uint32_t rows) {
+    if (lanes_per_row_log2(t, k) < 6) return 1;
+    const uint32_t steps = pieces_of(t, k) / 64;
+    if (steps < 3) return 1;
+    const uint32_t per_row = 1024 / (rows ? rows : 1);
+    uint32_t K = 1;
+    while (K < 8 && 2 * K <= per_row && 2 * K <= steps) K *= 2;
+    return K;
+}
 
 MvAttributes mv_attributes(int t) {
     switch (t) {
@@ -349,9 +374,28 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     DevInfo di;
     int rc = device_info(di);
     if (rc) return rc;
-    s.k_split = derived_k_split(t, k);
     const uint64_t rows = (uint64_t)n * batch;
+    s.k_split = derived_k_split(t, k, n);
     const uint32_t step = wave_step_values(t);
+    if (s.k_split > 1) {
+        // Skinny outputs, K waves per row group: max(4, K) waves per
+        // workgroup (one or two row groups of single rows; 4 waves measured
+        // 2-14% faster than 8 at K = 2 and up to 3% at K = 4), one round of
+        // row groups; LDS passes of the most whole wave steps that fit when
+        // x does not.
+        const uint32_t K = s.k_split;
+        uint32_t kc = k;
+        if (lds_bytes(t, m, k, k, K) > di.lds_max) {
+            kc = step;
+            while (kc + step < k && lds_bytes(t, m, k, kc + step, K) <= di.lds_max) kc += step;
+        }
+        s.k_chunk = kc;
+        s.rows_per_wave = 1;
+        s.waves_per_workgroup = K > 4 ? K : 4;
+        const uint32_t groups = s.waves_per_workgroup / K;
+        s.workgroups_per_batch = (n + groups - 1) / groups;
+        return 0;
+    }
     // LDS passes: one if the m staged rows fit, else the largest wave-step multiple that fits
     uint32_t kc = k;
     if (lds_bytes(t, m, k, k) > di.lds_max) {
@@ -451,16 +495,26 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     return 0;
 }
 
-// Checks that need no device (every field's range).
+// Checks that need no device (every field's range).  k_split may differ
+// from the derived one (the caller then chooses the numerics, e.g. to keep
+// the bits of an unsharded product on a row shard).
 int check_schedule_fields(int t, uint32_t k, const row_exact_schedule_t &s) {
-    const uint32_t ks = derived_k_split(t, k);
-    if (s.k_split != ks)
-        return fail(ROW_EXACT_ESCHEDULE, "schedule k_split (%u) must be %u for %s with k = %u", s.k_split, ks,
-                    type_name(t), k);
+    const uint32_t K = s.k_split;
+    if (!(K == 1 || K == 2 || K == 4 || K == 8))
+        return fail(ROW_EXACT_ESCHEDULE, "schedule k_split (%u) must be 1, 2, 4 or 8", K);
+    if (K > 1 && lanes_per_row_log2(t, k) < 6)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule k_split (%u): %s rows of k = %u (at most 32 pieces) are not split",
+                    K, type_name(t), k);
+    if (K > pieces_of(t, k) / 64 && K > 1)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule k_split (%u) exceeds the %u whole wave steps of a %s row of k = %u",
+                    K, pieces_of(t, k) / 64, type_name(t), k);
     if (!(s.rows_per_wave == 1 || s.rows_per_wave == 2 || s.rows_per_wave == 4))
         return fail(ROW_EXACT_ESCHEDULE, "schedule rows_per_wave (%u) must be 1, 2 or 4", s.rows_per_wave);
     if (s.waves_per_workgroup < 1 || s.waves_per_workgroup > 8)
         return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be in 1..=8", s.waves_per_workgroup);
+    if (s.waves_per_workgroup % K)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be a multiple of k_split (%u)",
+                    s.waves_per_workgroup, K);
     if (s.workgroups_per_batch < 1)
         return fail(ROW_EXACT_ESCHEDULE, "schedule workgroups_per_batch must be >= 1");
     const uint32_t step = wave_step_values(t);
@@ -472,7 +526,7 @@ int check_schedule_fields(int t, uint32_t k, const row_exact_schedule_t &s) {
 
 // Checks against the current device's limits.
 int check_schedule_device(int t, uint32_t k, uint32_t m, const row_exact_schedule_t &s, const DevInfo &di) {
-    const size_t l = lds_bytes(t, m, k, s.k_chunk);
+    const size_t l = lds_bytes(t, m, k, s.k_chunk, s.k_split);
     if (l > di.lds_max)
         return fail(ROW_EXACT_ESCHEDULE, "schedule needs %zu bytes of LDS, the device allows %zu", l, di.lds_max);
     return 0;
@@ -616,10 +670,12 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     {
         const uint64_t ahead = 4ull * 2 * 64 * sch.waves_per_workgroup;
         const bool dma_type = t == kQ6K;  // the types with a DMA staging path (Tr<T>::LOADS > 0)
-        a.x_dma = (a.nchunks == 1 && m == 1 && !norm && dma_type && k > ahead) ? 1u : 0u;
+        a.x_dma = (a.nchunks == 1 && m == 1 && !norm && dma_type && k > ahead && sch.k_split == 1) ? 1u : 0u;
     }
     a.row_scale = row_scale;
     a.row_scale_stride = m;
+    a.k_split = sch.k_split;
+    a.kp_offset = (uint32_t)lds_kp_offset(t, m, k, sch.k_chunk);
     {
         // items a wave walks in the single pass: its row groups x wave steps
         const uint32_t waves = sch.waves_per_workgroup;
@@ -630,7 +686,7 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     const uint64_t grid_x = (uint64_t)wgs * batch;
     if (grid_x > 0x7fffffffull)
         return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);
-    const size_t lds = lds_bytes(t, m, k, sch.k_chunk);
+    const size_t lds = lds_bytes(t, m, k, sch.k_chunk, sch.k_split);
     hipError_t e =
         mv_launcher(t)(a, m, nr, dim3((uint32_t)grid_x), dim3(64 * sch.waves_per_workgroup), lds, di.lds_max, stream);
     if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -53,6 +53,12 @@ struct MvArgs {
     // add + RMS norm runs on u = (x + r) * g with the rows' inverse RMS here.
     const double *row_scale;
     uint32_t row_scale_stride;
+    // Waves whose partial sums form one output (1, 2, 4 or 8; numerics: the
+    // row's wave steps are dealt round-robin over them and their sums added
+    // in a fixed order), and the LDS byte offset of their partials (32
+    // floats per wave) when > 1.
+    uint32_t k_split;
+    uint32_t kp_offset;
 };
 
 // The add + RMS statistics of the fused normalisation (norm_rows_kernel):

@@ -541,11 +541,11 @@ __device__ __forceinline__ float swap16_add(float x, float y) {
 
 constexpr int pow2ceil(int v) { return v <= 1 ? 1 : 2 * pow2ceil((v + 1) / 2); }
 
-// Sum each of the NR*M accumulators over the 64 lanes with the fixed tree
-// and store output (r, j) to y[j*yrs + row0 + r] when row0 + r < n.
-template <int M, int NR, int L>
-__device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *__restrict__ yb, uint32_t yrs,
-                                             uint32_t n, uint32_t row0, uint32_t lane, const RowScale &sc) {
+// Sum each of the NR*M accumulators over the L lanes of its row with the
+// fixed tree; the lane holding output o = r*M + j of slot `slot` (rows
+// slot*NR + r of the wave's group) calls emit(slot, o, sum).
+template <int M, int NR, int L, typename Emit>
+__device__ __forceinline__ void reduce_tree(const float (&acc)[NR][M], uint32_t lane, Emit &&emit) {
     // L lanes per weight row: slot lane / L of the wave holds rows
     // row0 + slot*NR + r.  The tree over a slot's lanes is the last log2(L)
     // levels of the 64-lane tree.
@@ -622,13 +622,53 @@ __device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *_
 #pragma unroll
         for (int a = 0; a < AN; ++a) {
             const uint32_t o = base + a;
-            if (o < (uint32_t)NA) {
-                const uint32_t r = o / M, j = o % M;
-                const uint32_t row = row0 + slot * NR + r;
-                if (row < n) yb[(uint64_t)j * yrs + row] = sc.apply(v[a], j);
-            }
+            if (o < (uint32_t)NA) emit(slot, o, v[a]);
         }
     }
+}
+
+// The tree, then output (r, j) of slot s to y[j*yrs + row0 + s*NR + r] when
+// that row is < n.
+template <int M, int NR, int L>
+__device__ __forceinline__ void reduce_store(const float (&acc)[NR][M], float *__restrict__ yb, uint32_t yrs,
+                                             uint32_t n, uint32_t row0, uint32_t lane, const RowScale &sc) {
+    reduce_tree<M, NR, L>(acc, lane, [&](uint32_t slot, uint32_t o, float v) {
+        const uint32_t r = o / M, j = o % M;
+        const uint32_t row = row0 + slot * NR + r;
+        if (row < n) yb[(uint64_t)j * yrs + row] = sc.apply(v, j);
+    });
+}
+
+// K-split reduction (K waves per row group): each wave's 64-lane tree sums
+// go to LDS (kp[wave][o], 32 floats per wave), and after a barrier the
+// group's first wave adds the K partials of each output by a fixed pairwise
+// tree over the split index, ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 +
+// p7)) truncated to K terms, then stores.  Every wave of the workgroup must
+// call it (it holds two barriers).
+template <int M, int NR>
+__device__ __forceinline__ void reduce_store_split(const float (&acc)[NR][M], float *__restrict__ kp, uint32_t K,
+                                                   uint32_t wave, uint32_t ws, bool active, float *__restrict__ yb,
+                                                   uint32_t yrs, uint32_t n, uint32_t row0, uint32_t lane,
+                                                   const RowScale &sc) {
+    constexpr int NA = NR * M;
+    static_assert(NA <= 32, "32 partials per wave");
+    reduce_tree<M, NR, 64>(acc, lane, [&](uint32_t, uint32_t o, float v) { kp[wave * 32 + o] = v; });
+    __syncthreads();
+    if (active && ws == 0 && lane < (uint32_t)NA) {
+        const float *p = kp + wave * 32 + lane;
+        float s;
+        if (K == 2) {
+            s = p[0] + p[32];
+        } else if (K == 4) {
+            s = (p[0] + p[32]) + (p[64] + p[96]);
+        } else {
+            s = ((p[0] + p[32]) + (p[64] + p[96])) + ((p[128] + p[160]) + (p[192] + p[224]));
+        }
+        const uint32_t r = lane / M, j = lane % M;
+        const uint32_t row = row0 + r;
+        if (row < n) yb[(uint64_t)j * yrs + row] = sc.apply(s, j);
+    }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------- x staging
@@ -1034,13 +1074,14 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
     }
 }
 
-// Pieces [pb, pe) of the NR rows, this lane's share (pb + lane, +64, ...),
-// with the next piece's loads issued before the current piece's math.
+// Pieces pb + lane, pb + lane + stride, ... below pe of the NR rows (stride
+// 64, or 64 K for the K-split, whose wave ws starts at pb + 64 ws), with the
+// next piece's loads issued before the current piece's math.
 template <int T, int M, int NR>
 __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *const (&R)[NR],
                                            const uint32_t (&o0)[NR], uint32_t pb, uint32_t pe, uint32_t vb,
                                            const float *__restrict__ xs, uint32_t XS, uint32_t k, uint32_t lane,
-                                           const float *__restrict__ sx, uint32_t SXS) {
+                                           const float *__restrict__ sx, uint32_t SXS, uint32_t stride) {
     using TR = Tr<T>;
     using Raw = typename TR::Raw;
     uint32_t p = pb + lane;
@@ -1049,13 +1090,13 @@ __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *c
 #pragma unroll
     for (int r = 0; r < NR; ++r) A[r] = load_walk<T>(R[r], o0[r], p, k);
     while (true) {
-        const uint32_t p1 = p + 64;
+        const uint32_t p1 = p + stride;
         const bool m1 = p1 < pe;
 #pragma unroll
         for (int r = 0; r < NR; ++r) B[r] = load_walk<T>(R[r], o0[r], m1 ? p1 : p, k);
         compute_piece<T, M, NR>(acc, A, p, vb, xs, XS, k, sx, SXS);
         if (!m1) break;
-        const uint32_t p2 = p1 + 64;
+        const uint32_t p2 = p1 + stride;
         const bool m2 = p2 < pe;
 #pragma unroll
         for (int r = 0; r < NR; ++r) A[r] = load_walk<T>(R[r], o0[r], m2 ? p2 : p1, k);
@@ -1231,7 +1272,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
     const uint8_t *__restrict__ Wb = a.W + wsel * a.batch_bytes;
     const uint32_t XS = a.xs_stride;
 
-    if (a.nchunks == 1) {
+    if (a.nchunks == 1 && a.k_split == 1) {
         // Single pass: the wave walks (row group, wave step) items of its
         // groups g0+wave, g0+wave+nwaves, ... with DEPTH items of loads in
         // flight.  The first DEPTH items are requested before x is staged.
@@ -1324,9 +1365,16 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             }
         }
     } else if constexpr (!SUB) {
-        // Several LDS passes over K (only for rows of more than 64 pieces, so
-        // 64 lanes per row): every wave of the workgroup works on one row
-        // group per round and all waves stage each pass together.
+        // Several LDS passes over K, or a K split (both only for rows of
+        // more than 64 pieces, so 64 lanes per row): every K waves of the
+        // workgroup work on one row group per round (wave ws of the K takes
+        // the row's wave steps ws, ws + K, ws + 2K, ..., in that order
+        // across the passes, so a pass of fewer than K steps leaves some of
+        // the K waves without work) and all waves stage each pass together.
+        const uint32_t K = a.k_split;
+        const uint32_t slots = nwaves / K;               // row groups per round
+        const uint32_t gs = wave / K, ws = wave - gs * K;  // group slot, split index
+        float *kp = (float *)((uint8_t *)xs + a.kp_offset);
         double *part = (double *)((uint8_t *)xs + a.norm_offset);
         const RowScale sc{NORM ? part : nullptr, a.row_scale ? a.row_scale + (uint64_t)b * a.row_scale_stride : nullptr,
                           a.k, a.eps};
@@ -1334,8 +1382,8 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         if constexpr (NORM)  // the pass loop's first barrier orders these writes before any store
             norm_partials<T, M, false>(part, nullptr, XS, xb, rb, a.g, (a.h && w == 0) ? a.h + b * a.xbs : nullptr,
                                        a.xrs, a.k, wave, nwaves, lane);
-        for (uint32_t base = g0; base < g1; base += nwaves) {
-            const uint32_t g = base + wave;
+        for (uint32_t base = g0; base < g1; base += slots) {
+            const uint32_t g = base + gs;
             const bool active = g < g1;
             float acc[NR][M];
             zero<M, NR>(acc);
@@ -1357,11 +1405,19 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                     stage_sx<T, M>(xs, XS, (float *)((uint8_t *)xs + a.sx_offset), a.sx_stride, ve - vb);
                     __syncthreads();
                 }
+                // the wave's first step in this pass: the first of the
+                // pass' wave steps s0, s0 + 1, ... with s = ws (mod K)
+                const uint32_t s0 = pb >> 6;
+                const uint32_t first = s0 + ((ws - s0) & (K - 1));
                 if (active)
-                    accumulate<T, M, NR>(acc, R, o0, pb, pe, vb, xs, XS, a.k, lane,
-                                         (const float *)((const uint8_t *)xs + a.sx_offset), a.sx_stride);
+                    accumulate<T, M, NR>(acc, R, o0, 64 * first, pe, vb, xs, XS, a.k, lane,
+                                         (const float *)((const uint8_t *)xs + a.sx_offset), a.sx_stride, 64 * K);
             }
-            if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane, sc);
+            if (K == 1) {
+                if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane, sc);
+            } else {
+                reduce_store_split<M, NR>(acc, kp, K, wave, ws, active, yb, a.yrs, a.n, g * NR, lane, sc);
+            }
         }
         // The walk leaves its last (unused) prefetch in flight; drain it
         // here, where nothing follows, so that the compiler's wait

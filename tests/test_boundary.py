@@ -196,7 +196,11 @@ def test_output_must_not_overlap_inputs():
 
 
 @pytest.mark.parametrize("sched,text", [
-    (Schedule(2, 1, 8, 1, 1 << 30), "k_split"),
+    (Schedule(3, 1, 8, 1, 1 << 30), "k_split (3) must be 1, 2, 4 or 8"),
+    (Schedule(16, 1, 8, 1, 1 << 30), "k_split (16) must be 1, 2, 4 or 8"),
+    (Schedule(4, 1, 8, 1, 1 << 30), "k_split (4) exceeds the 2 whole wave steps of a Q8_0 row of k = 4096"),
+    (Schedule(2, 1, 3, 1, 1 << 30), "waves_per_workgroup (3) must be a multiple of k_split (2)"),
+    (Schedule(2, 1, 8, 1, 1000), "k_chunk (1000) must be >= k (4096) or a multiple of 2048"),
     (Schedule(1, 3, 8, 1, 1 << 30), "rows_per_wave"),
     (Schedule(1, 1, 0, 1, 1 << 30), "waves_per_workgroup"),
     (Schedule(1, 1, 9, 1, 1 << 30), "waves_per_workgroup"),
@@ -206,6 +210,12 @@ def test_output_must_not_overlap_inputs():
 def test_invalid_schedule(sched, text):
     rc, msg = _mv(k=4096, schedule=sched)
     assert rc == -6 and text in msg, msg
+
+
+def test_k_split_needs_rows_of_64_lanes():
+    # F16 rows of k = 256 are 32 pieces (32 lanes per row): never split
+    rc, msg = _mv(wt=Weight.F16, k=256, schedule=Schedule(2, 1, 8, 1, 1 << 30))
+    assert rc == -6 and "k_split (2): F16 rows of k = 256 (at most 32 pieces) are not split" in msg, msg
 
 
 def test_null_schedule():

@@ -83,15 +83,21 @@ def test_repeat_bitwise(t, data):
         assert np.array_equal(bits(run_mv(t, d["Wd"], d["xd"], d["n"], d["k"], 5)), first)
 
 
-def _schedules(t, k):
-    step = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048, wl.F32: 256, wl.BF16: 512}[t]
+STEP = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048, wl.F32: 256, wl.BF16: 512}
+
+
+def _schedules(t, K):
+    """Packings with reduction split K: waves a multiple of K, LDS passes of
+    a multiple of K wave steps."""
+    step = STEP[t] * K
     out = []
     for nr in (1, 2, 4):
-        for waves, wgs in ((1, 1), (1, 1000), (4, 3), (8, 2), (8, 64), (3, 5)):
-            out.append(Schedule(1, nr, waves, wgs, 1 << 30))
-    out.append(Schedule(1, 2, 8, 4, step))      # several LDS passes
-    out.append(Schedule(1, 4, 2, 1, step))
-    out.append(Schedule(1, 1, 5, 7, 2 * step))
+        for waves, wgs in ((1, 1), (1, 1000), (4, 3), (8, 2), (8, 64), (3, 5), (6, 7)):
+            if waves % K == 0:
+                out.append(Schedule(K, nr, waves, wgs, 1 << 30))
+    out.append(Schedule(K, 2, 8, 4, step))      # several LDS passes
+    out.append(Schedule(K, 4, max(2, K), 1, step))
+    out.append(Schedule(K, 1, 8 if K > 1 else 5, 7, 2 * step))
     return out
 
 
@@ -101,7 +107,8 @@ def test_packing_is_inert(t, m, data):
     d = data[t]
     n, k = d["n"], d["k"]
     ref = bits(run_mv(t, d["Wd"], d["xd"], n, k, m))
-    for s in _schedules(t, k):
+    K = qfr.row_exact_schedule(t, n, k, m).k_split
+    for s in _schedules(t, K):
         got = bits(run_mv(t, d["Wd"], d["xd"], n, k, m, schedule=s))
         assert np.array_equal(got, ref), f"schedule {s} changed the bits"
 
@@ -171,10 +178,21 @@ def test_error_leaves_output_untouched(data):
 
 
 def test_default_schedule_properties():
+    """k_split is a function of (type, k, n): the largest power of two within
+    1024 / n, 8 and the row's whole 64-piece wave steps (1 below 3 steps),
+    the same for every m and batch; packing fields in range."""
     for t in TYPES:
         for k in (512 if t in wl.DENSE else 4096, 14336 if t in (wl.Q4_K, wl.Q6_K) else 8192):
-            splits = {qfr.row_exact_schedule(t, n, k, m).k_split for n in (64, 4096, 128256) for m in (1, 4, 8)}
-            assert splits == {1}
+            steps = k // STEP[t]
+            for n in (1, 5, 64, 200, 1023, 1024, 4096, 128256):
+                splits = {qfr.row_exact_schedule(t, n, k, m, batch).k_split for m in (1, 4, 8) for batch in (1, 3)}
+                assert len(splits) == 1, (t, k, n, splits)
+                K = splits.pop()
+                assert K in (1, 2, 4, 8) and K * n <= max(1024, n) and K <= max(1, steps)
+                if n >= 1024 or steps < 3:
+                    assert K == 1
+                else:
+                    assert 2 * K * n > 1024 or 2 * K > 8 or 2 * K > steps, (t, k, n, K)
             s = qfr.row_exact_schedule(t, 4096, k, 8)
             assert s.rows_per_wave in (1, 2, 4) and 1 <= s.waves_per_workgroup <= 8
 

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 # 512-thread workgroup requests ahead of the weights (4 per thread at
 # m = 2..4: 8192 values; 2 at m = 1: 4096).
 CASES = [(wl.Q8_0, 8832), (wl.Q4_K, 9216), (wl.Q6_K, 9216), (wl.F32, 8832)]
-N = 37
+N = 1031  # n >= 1024: one wave per output (no split), the path these cases stage for
 
 
 @pytest.mark.parametrize("t,k", CASES, ids=[f"{wl.TYPE_NAMES[t]}-k{k}" for t, k in CASES])
