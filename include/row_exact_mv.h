@@ -106,8 +106,9 @@ typedef struct {
  *                         wave steps, dividing waves_per_workgroup); outputs
  *                         then follow that value, e.g. to keep the bits of
  *                         an unsharded product on a row shard.
- *  rows_per_wave        : packing.  Weight rows a wave streams together,
- *                         sharing each input load: 1, 2 or 4.
+ *  rows_per_wave        : packing.  Weight rows a wave streams at once
+ *                         (each x value read from LDS serves all of them):
+ *                         1, 2 or 4.
  *  waves_per_workgroup  : packing.  1..8 (64..512 threads).
  *  workgroups_per_batch : packing.  Workgroups per batch entry; the grid
  *                         holds workgroups_per_batch x batch of them,

@@ -511,7 +511,7 @@ int check_schedule_fields(int t, uint32_t k, const row_exact_schedule_t &s) {
     if (!(s.rows_per_wave == 1 || s.rows_per_wave == 2 || s.rows_per_wave == 4))
         return fail(ROW_EXACT_ESCHEDULE, "schedule rows_per_wave (%u) must be 1, 2 or 4", s.rows_per_wave);
     if (s.waves_per_workgroup < 1 || s.waves_per_workgroup > 8)
-        return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be in 1..=8", s.waves_per_workgroup);
+        return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be 1 to 8", s.waves_per_workgroup);
     if (s.waves_per_workgroup % K)
         return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be a multiple of k_split (%u)",
                     s.waves_per_workgroup, K);
