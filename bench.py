@@ -60,6 +60,9 @@ def parse():
                     help="time the default schedule against pinned packings for the workloads named with "
                          "--sweep-workloads (default: the held-out shapes) and write the results to this JSON file")
     ap.add_argument("--sweep-workloads", default="", help="comma-separated workload names for --schedule-sweep")
+    ap.add_argument("--split-sweep", default="",
+                    help="write the skinny-output comparison (default schedule, its reduction split, against "
+                         "the best single-wave-row packing) to this JSON file")
     ap.add_argument("--profile-only", action="store_true",
                     help="launch the timed steps eagerly and exit (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -186,6 +189,10 @@ def main():
     if args.schedule_sweep:
         names = [v for v in args.sweep_workloads.split(",") if v] or None
         schedule_sweep(args.schedule_sweep, names)
+        return
+    if args.split_sweep:
+        names = [v for v in args.sweep_workloads.split(",") if v] or None
+        split_sweep(args.split_sweep, names)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the mat-vec shards by weight rows with no "
@@ -324,20 +331,22 @@ def main():
     # timed from Python in a loop of ctypes calls, next to the same loop over
     # an entry point that does nothing (ctypes' own cost).  The launches queue
     # behind a spin kernel, so the GPU never back-pressures the host.
+    # Each m gets a spin of its own and at most 200 queued launches, so the
+    # launch queue never fills (a full queue blocks the host on the GPU).
     host_us = {}
     reps_h = 200
-    with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(2e8))
-        t0 = time.perf_counter()
-        for r in range(reps_h):
-            lib.row_exact_launch_count()
-        floor = (time.perf_counter() - t0) / reps_h * 1e6
-        for m in ms:
+    t0 = time.perf_counter()
+    for r in range(reps_h):
+        lib.row_exact_launch_count()
+    floor = (time.perf_counter() - t0) / reps_h * 1e6
+    for m in ms:
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(2e8))
             t0 = time.perf_counter()
             for r in range(reps_h):
                 launch(i + r, m)
             host_us[f"m{m}"] = round((time.perf_counter() - t0) / reps_h * 1e6, 3)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     host_us["ctypes_floor"] = round(floor, 3)
 
     # Whole-job timing: graph replay of the same K steps (or eager with --eager).
@@ -698,6 +707,99 @@ def schedule_sweep(path, names=None):
             rec = {"workload": name, "m": m, "default": d.asdict(), "default_us": round(med[None], 3),
                    "best_pinned": cands[best_key].asdict(), "best_pinned_us": round(med[best_key], 3),
                    "default_over_best": round(med[None] / med[best_key], 4),
+                   "candidates_timed": len(timed)}
+            res.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+        del Wd
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
+def split_sweep(path, names=None):
+    """Skinny outputs: for every m of each workload, the default schedule
+    (whose reduction split is derived from (type, k, n)) against pinned
+    packings with the split at 1 (one wave per row; the bits then differ,
+    within the tolerance) and with the derived split: rows per wave 1 / 2,
+    1 / 2 / 4 / 8 waves per workgroup (multiples of the split), one round of
+    workgroups, the default's LDS pass.  Each timed as the mean of
+    back-to-back launches on cold weights; then the default and the best of
+    each split again, in five interleaved rounds, median per schedule."""
+    import ctypes
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import quantized_few_row_amd as qfr
+    import workloads as wl
+    names = names or list(wl.SKINNY)
+    lib = qfr.load_library()
+    stream = torch.cuda.Stream()
+    hs = stream.cuda_stream
+    res = []
+    for name in names:
+        w = wl.get(name)
+        t, n, k, batch = w.wtype, w.n, w.k, w.batch
+        xrs, xbs, yrs, ybs = w.strides(8)
+        st = qfr.Strides(xrs, xbs, yrs, ybs)
+        W = w.make_weights()
+        copies = max(2, int(np.ceil((1 << 30) / w.stored_weight_bytes)))
+        Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
+        wp = [Wd[c].data_ptr() for c in range(copies)]
+        xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        for m in w.ms:
+            _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, st)
+            y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
+            d = qfr.row_exact_schedule(t, n, k, m, batch)
+            cands = {}
+            for K in sorted({1, d.k_split}):
+                for nr in (1, 2):
+                    for wv in (1, 2, 4, 8):
+                        if wv % K:
+                            continue
+                        wgs = max(1, -(-n // (nr * wv // K)))
+                        cands[(K, nr, wv)] = qfr.Schedule(K, nr, wv, wgs, d.k_chunk)
+
+            def run(s, i):
+                if s is None:
+                    return lib.row_exact_mv(t, wp[i % copies], xd.data_ptr(), y.data_ptr(), n, k, m, batch,
+                                            ctypes.byref(st), hs)
+                return lib.row_exact_mv_scheduled(t, wp[i % copies], xd.data_ptr(), y.data_ptr(), n, k, m, batch,
+                                                  ctypes.byref(st), ctypes.byref(s), hs)
+
+            def mean_us(s, reps=100):
+                with torch.cuda.stream(stream):
+                    for i in range(3):
+                        run(s, i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda._sleep(int(2e6))
+                    e0.record(stream)
+                    for i in range(reps):
+                        run(s, i)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / reps
+
+            timed = {}
+            for key, s in cands.items():
+                with torch.cuda.stream(stream):
+                    rc = run(s, 0)
+                torch.cuda.synchronize()
+                if rc:  # over the device's limits (refused before launch)
+                    continue
+                timed[key] = mean_us(s)
+            best = {K: min((key for key in timed if key[0] == K), key=timed.get) for K in {key[0] for key in timed}}
+            rounds = {None: [], **{b: [] for b in best.values()}}
+            for _ in range(5):
+                for key in rounds:
+                    rounds[key].append(mean_us(cands[key] if key else None))
+            med = {key: statistics.median(v) for key, v in rounds.items()}
+            rec = {"workload": name, "m": m, "default": d.asdict(), "default_us": round(med[None], 3),
+                   "best_unsplit": cands[best[1]].asdict(), "best_unsplit_us": round(med[best[1]], 3),
+                   "best_derived_split": cands[best[d.k_split]].asdict(),
+                   "best_derived_split_us": round(med[best[d.k_split]], 3),
+                   "unsplit_over_default": round(med[best[1]] / med[None], 4),
                    "candidates_timed": len(timed)}
             res.append(rec)
             print(json.dumps(rec), file=sys.stderr, flush=True)

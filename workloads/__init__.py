@@ -238,7 +238,20 @@ WORKLOADS: List[Workload] = [
     Workload("q4_k_1024x2816", Q4_K, 1024, 2816, 1, (1, 2, 3, 4), 10),
     Workload("q8_0_2816x2112", Q8_0, 2816, 2112, 1, (1, 2, 3, 4), 11),
 ]
+# skinny outputs (few rows, long rows): the reduction split across waves
+# (k_split > 1) against single-wave rows; a router-like F16 64 x 4096, a
+# single-output F16 head, and quantized projections of 32..128 rows
+SKINNY_WORKLOADS: List[Workload] = [
+    Workload("f16_64x4096", F16, 64, 4096, 1, (1, 4, 8), 12),
+    Workload("f16_1x8192", F16, 1, 8192, 1, (1, 4, 8), 13),
+    Workload("bf16_128x8192", BF16, 128, 8192, 1, (1, 4, 8), 14),
+    Workload("q8_0_128x16384", Q8_0, 128, 16384, 1, (1, 4, 8), 15),
+    Workload("q4_k_64x14336", Q4_K, 64, 14336, 1, (1, 4, 8), 16),
+    Workload("q6_k_32x14336", Q6_K, 32, 14336, 1, (1, 4, 8), 17),
+]
+WORKLOADS += SKINNY_WORKLOADS
 HELD_OUT = ("q4_k_1024x2816", "q8_0_2816x2112")
+SKINNY = tuple(w.name for w in SKINNY_WORKLOADS)
 BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
 
 
