@@ -178,3 +178,22 @@ def test_split_fused_norm_one_kernel_equals_two_launches(t):
         assert np.array_equal(bits(h), href[:m * k].view(np.int32)), f"m={m}: h"
         check_tolerance(y1.cpu().numpy().reshape(1, m, n), yref[:, :m], a[:, :m], f"m={m}")
         assert np.array_equal(bits(y1), bits(y2)), f"m={m}: one kernel and two launches differ"
+
+
+@pytest.mark.parametrize("t", [wl.Q8_0, wl.Q6_K, wl.Q5_0], ids=["Q8_0", "Q6_K", "Q5_0"])
+def test_split_two_byte_aligned_weights(t, data):
+    """W 2 bytes past a 4-byte boundary (the page accepts any even address
+    for these types) with the split: the same bits as W aligned, every m."""
+    d = data[t]
+    k, n = d["k"], 64
+    rb = qfr.row_exact_row_bytes(t, k)
+    raw = d["W"].ravel()[:n * rb]
+    buf = torch.zeros(raw.size + 32, dtype=torch.uint8, device="cuda:0")
+    buf[2:2 + raw.size].copy_(torch.from_numpy(raw.copy()))
+    Wo = buf[2:2 + raw.size]
+    assert Wo.data_ptr() % 4 == 2
+    assert qfr.row_exact_schedule(t, n, k, 1).k_split > 1
+    for m in (1, 5, 8):
+        y = run_mv(t, Wo, d["xd"], n, k, m)
+        check_tolerance(y.cpu().numpy().reshape(m, n), d["y"][:m, :n], d["a"][:m, :n], f"m={m}")
+        assert np.array_equal(bits(y), bits(run_mv(t, d["Wd"], d["xd"], n, k, m))), f"m={m}: differs from aligned W"
