@@ -33,6 +33,13 @@ SHAPES = {
     wl.F32: (69, 1028),    # 257 pieces of 4 values: 4 wave steps and one piece
     wl.BF16: (77, 1028),   # as F16
 }
+# Rows of 5 wave steps and a ragged 60-piece tail (380 pieces), long enough
+# for packings with several LDS passes at every m and, with n < 128, a
+# reduction split of 4 waves.
+SHAPES64 = {
+    wl.F16: (77, 3040), wl.Q8_0: (70, 12160), wl.Q4_K: (67, 24320), wl.Q6_K: (41, 24320),
+    wl.Q5_0: (53, 12160), wl.F32: (69, 1520), wl.BF16: (77, 3040),
+}
 TYPES = list(SHAPES)
 IDS = [wl.TYPE_NAMES[t] for t in TYPES]
 
@@ -111,6 +118,41 @@ def test_packing_is_inert(t, m, data):
     for s in _schedules(t, K):
         got = bits(run_mv(t, d["Wd"], d["xd"], n, k, m, schedule=s))
         assert np.array_equal(got, ref), f"schedule {s} changed the bits"
+
+
+@pytest.mark.parametrize("t", TYPES, ids=IDS)
+def test_several_passes_and_split(t):
+    """Rows of several wave steps and a ragged tail: tolerance and row
+    exactness at m = 1, 3, 8, every packing that fits (several LDS passes
+    included, with the derived split) bitwise equal; for the 2-byte-aligned
+    types also W 2 bytes past a 4-byte boundary, in one and several passes."""
+    n, k = SHAPES64[t]
+    W = wl.weights(t, n, k, seed=330 + t)
+    x = wl.activations(8, k, seed=430 + t)
+    Wd, xd = to_dev(W.ravel()), to_dev(x.ravel())
+    ref, a = oracle.matvec(t, W, x, n, k, 8)
+    ones = [bits(run_mv(t, Wd, xd[j * k:], n, k, 1)) for j in range(8)]
+    for m in (1, 3, 8):
+        y = run_mv(t, Wd, xd, n, k, m)
+        check_tolerance(y.cpu().numpy().reshape(m, n), ref[0, :m], a[0, :m], f"m={m}")
+        yb = bits(y)
+        for j in range(m):
+            assert np.array_equal(yb.reshape(m, n)[j], ones[j]), f"m={m} row {j} differs from its m=1 result"
+        sd = qfr.row_exact_schedule(t, n, k, m)
+        K = sd.k_split
+        assert K == 4, K
+        kc_max = 1 << 30 if sd.k_chunk >= k else sd.k_chunk  # the largest pass that fits at this m
+        for s in _schedules(t, K):
+            if s.k_chunk <= kc_max:
+                assert np.array_equal(bits(run_mv(t, Wd, xd, n, k, m, schedule=s)), yb), f"m={m}: schedule {s}"
+        if t in (wl.Q8_0, wl.Q6_K, wl.Q5_0):
+            raw = W.ravel()
+            buf = torch.zeros(raw.size + 32, dtype=torch.uint8, device="cuda:0")
+            buf[2:2 + raw.size].copy_(torch.from_numpy(raw.copy()))
+            Wo = buf[2:2 + raw.size]
+            for s in (None, Schedule(K, 2, 8, 4, STEP[t])):
+                got = bits(run_mv(t, Wo, xd, n, k, m, schedule=s))
+                assert np.array_equal(got, yb), f"m={m}: 2-byte-aligned W, schedule {s}"
 
 
 @pytest.mark.parametrize("t", TYPES, ids=IDS)
