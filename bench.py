@@ -605,8 +605,11 @@ def sweep(path, steps):
                 us2 = span_us(lambda i: qfr.row_exact_mv_add_rmsnorm_ws(t, Wd[i % copies], xd, rd, gd, 1e-5, hd, y, n,
                                                                        k, m, batch, s, work=work))
                 us0 = span_us(lambda i: qfr.row_exact_mv(t, Wd[i % copies], xd, y, n, k, m, batch, s))
+                # the residual form (h := r, layer output x, w = w2 := g), same work buffer
+                us3 = span_us(lambda i: qfr.row_exact_mv_residual_rmsnorm_ws(
+                    t, Wd[i % copies], rd, xd, gd, None, gd, 1e-5, 1e-5, hd, y, n, k, m, batch, s, work=work))
                 res[-1].update({"one_kernel_us": round(us, 3), "two_launch_us": round(us2, 3),
-                                "plain_product_us": round(us0, 3)})
+                                "plain_product_us": round(us0, 3), "residual_two_launch_us": round(us3, 3)})
             print(json.dumps(res[-1]), file=sys.stderr, flush=True)
         del Wd
         torch.cuda.empty_cache()

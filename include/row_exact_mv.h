@@ -247,6 +247,38 @@ int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const floa
                                 const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
                                 hipStream_t stream);
 
+/* The product whose input is a residual RMS normalisation (nuvec-core
+ * 0.6.0, src/gpu.rs, residual_rms_norm: the residual stream plus the RMS
+ * normalisation of a layer output, optionally scaled, and that sum's own
+ * RMS normalisation for the next projection), as two launches on `stream`
+ * with a caller's work buffer.  For every batch entry b and input row j,
+ * over its k values:
+ *   hs = (h + x / sqrt(mean(x^2) + eps) * w) * c
+ *   y[b, j, :] = W[b] . (hs / sqrt(mean(hs^2) + eps2) * w2)
+ * Reading of the page (its kernel is not shown): w, c, w2 are k-vectors
+ * (NULL: 1, no scaling, 1); the first normalisation's value is rounded to
+ * float32 once, the addition and the scaling are float32 operations; both
+ * statistics are float64 sums in one fixed order.  The first kernel writes
+ * hs to hout (NULL: not written), u = hs * w2 and each row's inverse RMS of
+ * hs into `work`; the plain mat-vec then runs on u, every output scaled by
+ * its row's value, so outputs are row-exact as row_exact_mv's.
+ *  h, x       : device, the layout of x in row_exact_mv (strides), 16-byte
+ *               aligned; h is the residual stream, x the layer output.
+ *  w, c, w2   : device, k floats each, 16-byte aligned, or NULL.
+ *  eps, eps2  : finite, >= 0.
+ *  hout       : device, x's layout, 16-byte aligned, or NULL; may be h
+ *               itself (updated in place) but must not overlap anything else.
+ *  work       : as row_exact_mv_add_rmsnorm_ws (ROW_EXACT_NORM_WORK_BYTES).
+ * Other arguments as row_exact_mv.  Errors: as row_exact_mv, plus
+ * ROW_EXACT_EARG (NULL h or work, eps or eps2 out of range, work_bytes too
+ * small), ROW_EXACT_EALIGN, and ROW_EXACT_EALIAS (y against h, w, c, w2;
+ * hout against everything but h; work against every operand). */
+int row_exact_mv_residual_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *h, const float *x,
+                                     const float *w, const float *c, const float *w2, float eps, float eps2,
+                                     float *hout, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                                     const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
+                                     hipStream_t stream);
+
 /* Bytes of the scratch array behind row_exact_mv_add_rmsnorm_noalloc, per
  * GPU: it serves calls whose ROW_EXACT_NORM_WORK_BYTES(k, m, batch) is at
  * most this. */

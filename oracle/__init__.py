@@ -67,6 +67,9 @@ def _load() -> ctypes.CDLL:
         lib.oracle_dequant.argtypes = [ctypes.c_int, P, u32, u32, P]
         lib.oracle_matvec_rows.restype = ctypes.c_int
         lib.oracle_matvec_rows.argtypes = [ctypes.c_int, P, P, u32, u32, u32, u32, u32, u32, u32, u32, P, P]
+        lib.oracle_mv_residual_rmsnorm.restype = ctypes.c_int
+        lib.oracle_mv_residual_rmsnorm.argtypes = [ctypes.c_int, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float,
+                                                   u32, u32, u32, u32, u32, u32, P, P, P, P]
         lib.oracle_mv_add_rmsnorm.restype = ctypes.c_int
         lib.oracle_mv_add_rmsnorm.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, u32, u32, u32, u32, u32,
                                               u32, P, P, P, P]
@@ -203,3 +206,39 @@ def mv_add_rmsnorm(wtype: int, W: np.ndarray, x: np.ndarray, r: np.ndarray, g: O
     if rc != 0:
         raise ValueError(f"oracle_mv_add_rmsnorm failed ({rc})")
     return h, xn, y, a
+
+
+def mv_residual_rmsnorm(wtype: int, W: np.ndarray, h: np.ndarray, x: np.ndarray, w: Optional[np.ndarray],
+                        c: Optional[np.ndarray], w2: Optional[np.ndarray], eps: float, eps2: float, n: int, k: int,
+                        m: int, batch: int = 1, x_row_stride: Optional[int] = None,
+                        x_batch_stride: int = 0) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Float64 reference of the product whose input is the residual RMS
+    normalisation: ``hs = (h + rms_norm(x) * w) * c`` (float32 steps) and
+    ``xn = rms_norm(hs) * w2``.  Returns ``(hs, xn, y, a)``; ``hs`` (float32)
+    in x's flat layout, ``xn`` [batch, m, k] float64, ``y`` and ``a``
+    [batch, m, n].  ``w``, ``c``, ``w2``: k float32 values or None (1, no
+    scaling, 1)."""
+    lib = _load()
+    xrs = k if x_row_stride is None else x_row_stride
+    Wb = np.ascontiguousarray(W, dtype=np.uint8).ravel()
+    hf = np.ascontiguousarray(h, dtype=np.float32).ravel()
+    xf = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    need_x = (batch - 1) * x_batch_stride + (m - 1) * xrs + k
+    if Wb.size < row_bytes(wtype, k) * n * batch or xf.size < need_x or hf.size < need_x:
+        raise ValueError("oracle.mv_residual_rmsnorm: buffers too small")
+    vecs = []
+    for v in (w, c, w2):
+        vf = None if v is None else np.ascontiguousarray(v, dtype=np.float32).ravel()
+        if vf is not None and vf.size < k:
+            raise ValueError("oracle.mv_residual_rmsnorm: weight vector too small")
+        vecs.append(vf)
+    hs = np.full(xf.size, np.nan, dtype=np.float32)
+    xn = np.empty((batch, m, k), dtype=np.float64)
+    y = np.empty((batch, m, n), dtype=np.float64)
+    a = np.empty((batch, m, n), dtype=np.float64)
+    rc = lib.oracle_mv_residual_rmsnorm(wtype, _ptr(Wb), _ptr(hf), _ptr(xf),
+                                        *[None if v is None else _ptr(v) for v in vecs], eps, eps2, n, k, m, batch,
+                                        xrs, x_batch_stride, _ptr(hs), _ptr(xn), _ptr(y), _ptr(a))
+    if rc != 0:
+        raise ValueError(f"oracle_mv_residual_rmsnorm failed ({rc})")
+    return hs, xn, y, a

@@ -293,6 +293,67 @@ int oracle_matvec_gather(int type, const uint8_t *W, uint32_t num_experts, const
     return 0;
 }
 
+/* The product with a residual RMS normalisation producing its input
+ * (nuvec-core 0.6.0, src/gpu.rs, residual_rms_norm: the residual stream plus
+ * the RMS normalisation of a layer output, optionally scaled, then that sum's
+ * own RMS normalisation for the next projection).  For every batch b and
+ * input row j, over the k values v of the row (h, x and hout share the
+ * layout b*xbs + j*xrs + v):
+ *   s1      = sum_v x[v]^2                                  (float64, v in order)
+ *   t[v]    = x[v] / sqrt(s1 / k + eps) * w[v]              (float64, rounded once to float32; w NULL: 1)
+ *   hs[v]   = h[v] + t[v]                                   (float32 addition)
+ *   hs[v]   = hs[v] * c[v]                                  (float32 multiplication; c NULL: skipped)
+ *   s2      = sum_v hs[v]^2                                 (float64, v in order)
+ *   xn[v]   = hs[v] / sqrt(s2 / k + eps2) * w2[v]           (float64; w2 NULL: 1)
+ *   y[(b*m + j)*n + i] = sum_v Wd[b*n + i][v] * xn[v]       (float64)
+ *   a[...]             = sum_v |Wd[b*n + i][v] * xn[v]|
+ * hout (= hs) is written in x's layout, xn dense [batch][m][k]. */
+int oracle_mv_residual_rmsnorm(int type, const uint8_t *W, const float *h, const float *x, const float *w,
+                               const float *c, const float *w2, float eps, float eps2, uint32_t n, uint32_t k,
+                               uint32_t m, uint32_t batch, uint32_t xrs, uint32_t xbs, float *hout, double *xn,
+                               double *y, double *a) {
+    if (!k_ok(type, k) || m == 0 || n == 0 || batch == 0) return -1;
+    uint64_t rb = oracle_row_bytes(type, k);
+    float *wd = (float *)malloc(sizeof(float) * k);
+    if (!wd) return -2;
+    for (uint32_t b = 0; b < batch; ++b) {
+        for (uint32_t j = 0; j < m; ++j) {
+            size_t off = (size_t)b * xbs + (size_t)j * xrs;
+            double *xr = xn + ((size_t)b * m + j) * k;
+            double s1 = 0.0;
+            for (uint32_t v = 0; v < k; ++v) s1 += (double)x[off + v] * (double)x[off + v];
+            double rms1 = sqrt(s1 / (double)k + (double)eps);
+            double s2 = 0.0;
+            for (uint32_t v = 0; v < k; ++v) {
+                float t = (float)((double)x[off + v] / rms1 * (w ? (double)w[v] : 1.0));
+                float hs = h[off + v] + t;
+                if (c) hs = hs * c[v];
+                hout[off + v] = hs;
+                s2 += (double)hs * (double)hs;
+            }
+            double rms2 = sqrt(s2 / (double)k + (double)eps2);
+            for (uint32_t v = 0; v < k; ++v) xr[v] = (double)hout[off + v] / rms2 * (w2 ? (double)w2[v] : 1.0);
+        }
+        for (uint32_t i = 0; i < n; ++i) {
+            const uint8_t *row = W + rb * ((uint64_t)b * n + i);
+            for (uint32_t v = 0; v < k; ++v) wd[v] = oracle_weight(type, row, v);
+            for (uint32_t j = 0; j < m; ++j) {
+                const double *xr = xn + ((size_t)b * m + j) * k;
+                double sy = 0.0, sa = 0.0;
+                for (uint32_t v = 0; v < k; ++v) {
+                    double p = (double)wd[v] * xr[v];
+                    sy += p;
+                    sa += fabs(p);
+                }
+                y[((size_t)b * m + j) * n + i] = sy;
+                a[((size_t)b * m + j) * n + i] = sa;
+            }
+        }
+    }
+    free(wd);
+    return 0;
+}
+
 /* The product with a fused add + RMS normalisation of its input (nuvec-core
  * 0.6.0, src/gpu.rs, add_rms_norm: the sum x + r and its RMS normalisation
  * with weight g).  For every batch b and input row j, over the k values v of

@@ -125,6 +125,9 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_mv_add_rmsnorm_ws.restype = ctypes.c_int
     lib.row_exact_mv_add_rmsnorm_ws.argtypes = [ctypes.c_int, P, P, P, P, ctypes.c_float, P, P, u32, u32, u32, u32, SP,
                                                 P, u64, P]
+    lib.row_exact_mv_residual_rmsnorm_ws.restype = ctypes.c_int
+    lib.row_exact_mv_residual_rmsnorm_ws.argtypes = [ctypes.c_int, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, P,
+                                                     P, u32, u32, u32, u32, SP, P, u64, P]
     lib.row_exact_schedule.restype = ctypes.c_int
     lib.row_exact_schedule.argtypes = [ctypes.c_int, u32, u32, u32, u32, SchP]
     lib.row_exact_row_bytes.restype = u64
@@ -298,6 +301,52 @@ def row_exact_mv_add_rmsnorm_ws(wt: int, W: Any, x: Any, r: Any, g: Any, eps: fl
     wp, wlen = _ptr_and_bytes(work, "work")
     _norm_call("row_exact_mv_add_rmsnorm_ws", wt, W, x, r, g, eps, h, y, n, k, m, batch, strides, stream,
                (wp, need if wlen is None else wlen))
+
+def _work_buffer(need: int, work: Any, stream: Any) -> Tuple[int, int]:
+    """(pointer, bytes) of a work buffer: the caller's, or one from torch's
+    caching allocator on the call's stream."""
+    if work is None:
+        # torch's caching allocator reuses a block only after the stream it was
+        # taken on has passed its last use, so the buffer is taken on the
+        # call's own stream (a raw handle cannot be given to torch)
+        if isinstance(stream, int):
+            raise ValueError("pass work explicitly when the stream is a raw handle")
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            work = torch.empty(need, dtype=torch.uint8, device=s.device)
+    wp, wlen = _ptr_and_bytes(work, "work")
+    return wp, need if wlen is None else wlen
+
+
+def row_exact_mv_residual_rmsnorm_ws(wt: int, W: Any, h: Any, x: Any, w: Any, c: Any, w2: Any, eps: float,
+                                     eps2: float, hout: Any, y: Any, n: int, k: int, m: int, batch: int = 1,
+                                     strides: Optional[Strides] = None, work: Any = None,
+                                     stream: Any = None) -> None:
+    """Enqueue ``hs = (h + x / sqrt(mean(x^2) + eps) * w) * c`` (written to
+    ``hout`` unless None; ``hout`` may be ``h``) and
+    ``y = W . (hs / sqrt(mean(hs^2) + eps2) * w2)`` per input row (see
+    ``row_exact_mv_residual_rmsnorm_ws``); ``w``, ``c``, ``w2`` may be None.
+    ``work`` as in :func:`row_exact_mv_add_rmsnorm_ws`."""
+    wt = Weight(wt)
+    lib = load_library()
+    _dtype_check(wt, W, x, y)
+    _size_check(wt, W, x, y, n, k, m, batch, strides)
+    _, xb, _ = row_exact_required_bytes(wt, n, k, m, batch, strides)
+    for t, need, name in ((h, xb, "h"), (hout, xb, "hout"), (w, 4 * k, "w"), (c, 4 * k, "c"), (w2, 4 * k, "w2")):
+        if t is None:
+            continue
+        _, have = _ptr_and_bytes(t, name)
+        if have is not None and have < need:
+            raise ValueError(f"{name} holds {have} bytes, needs {need}")
+    wp, wlen = _work_buffer(norm_work_bytes(k, m, batch), work, stream)
+    ptr = lambda t, name: None if t is None else _ptr_and_bytes(t, name)[0]
+    sp = ctypes.byref(strides) if strides is not None else None
+    _check(lib.row_exact_mv_residual_rmsnorm_ws(int(wt), ptr(W, "weight"), ptr(h, "h"), ptr(x, "input"), ptr(w, "w"),
+                                                ptr(c, "c"), ptr(w2, "w2"), float(eps), float(eps2), ptr(hout, "hout"),
+                                                ptr(y, "output"), n, k, m, batch, sp, wp, wlen,
+                                                _stream_handle(stream)))
+
 
 def row_exact_mv_add_rmsnorm_noalloc(wt: int, W: Any, x: Any, r: Any, g: Any, eps: float, h: Any, y: Any, n: int,
                                      k: int, m: int, batch: int = 1, strides: Optional[Strides] = None,

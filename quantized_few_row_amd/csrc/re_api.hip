@@ -851,6 +851,74 @@ int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const
     return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, nullptr, ptr);
 }
 
+int row_exact_mv_residual_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *h, const float *x,
+                                     const float *w, const float *c, const float *w2, float eps, float eps2,
+                                     float *hout, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+                                     const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
+                                     hipStream_t stream) {
+    g_err.clear();
+    int rc = check_shape((int)wt, n, k, m, batch);
+    if (rc) return rc;
+    // the product's checks with x as its input (h and hout share x's layout)
+    const row_exact_strides_t s = resolve_strides(strides, m, n, k);
+    uint64_t wb = 0, xb = 0, yb = 0;
+    rc = validate_mv((int)wt, W, x, y, n, k, m, batch, s, wb, xb, yb, nullptr, 0);
+    if (rc) return rc;
+    if (!h) return fail(ROW_EXACT_EARG, "h must be a non-NULL device pointer");
+    if (!(eps >= 0.0f) || eps > 3.4e38f || !(eps2 >= 0.0f) || eps2 > 3.4e38f)
+        return fail(ROW_EXACT_EARG, "eps and eps2 must be finite and >= 0");
+    if ((uintptr_t)h % 16 || (uintptr_t)w % 16 || (uintptr_t)c % 16 || (uintptr_t)w2 % 16 || (uintptr_t)hout % 16)
+        return fail(ROW_EXACT_EALIGN, "h, w, c, w2 and hout must be 16-byte aligned");
+    const uint64_t vb = 4ull * k;
+    const uintptr_t yp = (uintptr_t)y;
+    if (overlap(yp, yb, (uintptr_t)h, xb) || (w && overlap(yp, yb, (uintptr_t)w, vb)) ||
+        (c && overlap(yp, yb, (uintptr_t)c, vb)) || (w2 && overlap(yp, yb, (uintptr_t)w2, vb)))
+        return fail(ROW_EXACT_EALIAS, "y overlaps h, w, c or w2");
+    if (hout) {
+        const uintptr_t hp = (uintptr_t)hout;
+        if (overlap(hp, xb, (uintptr_t)x, xb) || overlap(hp, xb, (uintptr_t)W, wb) || overlap(hp, xb, yp, yb) ||
+            (w && overlap(hp, xb, (uintptr_t)w, vb)) || (c && overlap(hp, xb, (uintptr_t)c, vb)) ||
+            (w2 && overlap(hp, xb, (uintptr_t)w2, vb)) || (hout != h && overlap(hp, xb, (uintptr_t)h, xb)))
+            return fail(ROW_EXACT_EALIAS, "hout overlaps x, W, y, w, c, w2 or (other than exactly) h");
+    }
+    if (!work) return fail(ROW_EXACT_EARG, "work must be a non-NULL device pointer");
+    if ((uintptr_t)work % 16) return fail(ROW_EXACT_EALIGN, "work must sit on a 16-byte boundary");
+    const uint64_t need = norm_work_bytes(k, m, batch);
+    if (work_bytes < need)
+        return fail(ROW_EXACT_EARG, "work holds %llu bytes, the call needs %llu", (unsigned long long)work_bytes,
+                    (unsigned long long)need);
+    const uintptr_t wp = (uintptr_t)work;
+    if (overlap(wp, need, (uintptr_t)W, wb) || overlap(wp, need, (uintptr_t)x, xb) ||
+        overlap(wp, need, (uintptr_t)h, xb) || overlap(wp, need, yp, yb) ||
+        (hout && overlap(wp, need, (uintptr_t)hout, xb)) || (w && overlap(wp, need, (uintptr_t)w, vb)) ||
+        (c && overlap(wp, need, (uintptr_t)c, vb)) || (w2 && overlap(wp, need, (uintptr_t)w2, vb)))
+        return fail(ROW_EXACT_EALIAS, "work overlaps W, x, h, hout, w, c, w2 or y");
+    ResidualArgs ra;
+    ra.h = h;
+    ra.x = x;
+    ra.w = w;
+    ra.c = c;
+    ra.w2 = w2;
+    ra.hout = hout;
+    ra.u = (float *)work;
+    ra.inv = (double *)((uint8_t *)work + (((uint64_t)batch * m * k * sizeof(float) + 255) & ~255ull));
+    ra.xbs = s.x_batch_stride;
+    ra.xrs = s.x_row_stride;
+    ra.k = k;
+    ra.m = m;
+    ra.eps = eps;
+    ra.eps2 = eps2;
+    hipError_t e = launch_residual_rows(ra, batch, stream);
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    row_exact_strides_t su;
+    su.x_row_stride = k;
+    su.x_batch_stride = m * k;
+    su.y_row_stride = s.y_row_stride;
+    su.y_batch_stride = s.y_batch_stride;
+    return run((int)wt, W, ra.u, y, n, k, m, batch, &su, nullptr, stream, nullptr, 0, nullptr, ra.inv);
+}
+
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                        row_exact_schedule_t *out) {
     g_err.clear();

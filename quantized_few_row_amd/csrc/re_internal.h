@@ -74,6 +74,21 @@ struct NormArgs {
 };
 hipError_t launch_norm_rows(const NormArgs &a, uint32_t batch, hipStream_t s);
 
+// The residual RMS normalisation's prologue kernel: per (batch entry, input
+// row), hs = (h + rms_norm(x) * w) * c written to hout (or NULL), u = hs * w2
+// and the inverse RMS of hs (with eps2).
+struct ResidualArgs {
+    const float *h, *x;           // the product's x layout
+    const float *w, *c, *w2;      // k values each, or NULL (1, no scaling, 1)
+    float *hout;                  // hs in the same layout, or NULL
+    float *u;                     // contiguous [batch][m][k]
+    double *inv;                  // [batch][m]
+    uint64_t xbs;
+    uint32_t xrs, k, m;
+    float eps, eps2;
+};
+hipError_t launch_residual_rows(const ResidualArgs &a, uint32_t batch, hipStream_t s);
+
 struct DqArgs {
     const uint8_t *W;
     float *out;

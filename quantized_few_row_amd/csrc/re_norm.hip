@@ -61,7 +61,95 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(const NormArgs a) {
     if (v == 0) a.inv[(uint64_t)b * a.m + j] = RowScale::inv_rms(part, a.k, a.eps);
 }
 
+// The workgroup's sum of the 256 virtual lanes' float64 partials: each
+// wave's 64 by the xor tree over masks 32, 16, ..., 1, the four wave sums as
+// (s0 + s1) + (s2 + s3); every thread gets 1 / sqrt(sum / k + eps).
+__device__ __forceinline__ double block_inv_rms(double ss, double *part, uint32_t lane, uint32_t wave, uint32_t k,
+                                                float eps) {
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) ss += shfl_xor_d(ss, msk);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    const double inv = RowScale::inv_rms(part, k, eps);
+    __syncthreads();  // part is reused
+    return inv;
+}
+
+// The prologue of the residual RMS normalisation (nuvec-core 0.6.0,
+// src/gpu.rs, residual_rms_norm: the residual stream plus the RMS
+// normalisation of a layer output, optionally scaled, and that sum's own RMS
+// normalisation), 256 threads per (batch entry, input row).  Both statistics
+// are summed in float64 in the order of norm_rows_kernel.  Per value:
+// t = (float)(x * inv1 * w) in float64, hs = h + t and hs = hs * c in
+// float32, u = hs * w2 in float32; the product then scales every output by
+// the row's inverse RMS of hs.
+__global__ void __launch_bounds__(256) residual_rows_kernel(const ResidualArgs a) {
+    const uint32_t b = blockIdx.x / a.m, j = blockIdx.x - b * a.m;
+    const uint32_t v = threadIdx.x, lane = v & 63u, wave = v >> 6;
+    const uint64_t o = (uint64_t)b * a.xbs + (uint64_t)j * a.xrs;
+    const float *__restrict__ xr = a.x + o;
+    const float *__restrict__ hr = a.h + o;
+    float *__restrict__ ho = a.hout ? a.hout + o : nullptr;
+    float *__restrict__ ur = a.u + ((uint64_t)b * a.m + j) * a.k;
+    const uint32_t n4 = a.k >> 2;
+    __shared__ double part[4];
+    double s1 = 0.0;
+    for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
+        f32x4 xv[kChunksAhead];
+#pragma unroll
+        for (int c = 0; c < kChunksAhead; ++c) {
+            const uint32_t q = q0 + 256u * c;
+            if (q < n4) xv[c] = *(const f32x4 *)(xr + 4 * q);
+        }
+#pragma unroll
+        for (int c = 0; c < kChunksAhead; ++c)
+            if (q0 + 256u * c < n4) s1 = fold4(s1, xv[c]);
+    }
+    const double inv1 = block_inv_rms(s1, part, lane, wave, a.k, a.eps);
+    double s2 = 0.0;
+    for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
+        f32x4 xv[kChunksAhead], hv[kChunksAhead];
+#pragma unroll
+        for (int c = 0; c < kChunksAhead; ++c) {
+            const uint32_t q = q0 + 256u * c;
+            if (q < n4) {
+                xv[c] = *(const f32x4 *)(xr + 4 * q);
+                hv[c] = *(const f32x4 *)(hr + 4 * q);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunksAhead; ++c) {
+            const uint32_t q = q0 + 256u * c;
+            if (q < n4) {
+                const f32x4 wv = a.w ? *(const f32x4 *)(a.w + 4 * q) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+                f32x4 hs;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = (float)((double)xv[c][e] * inv1 * (double)wv[e]);
+                    hs[e] = hv[c][e] + t;
+                }
+                if (a.c) {
+                    const f32x4 cv = *(const f32x4 *)(a.c + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hs[e] = hs[e] * cv[e];
+                }
+                if (ho) *(f32x4 *)(ho + 4 * q) = hs;
+                s2 = fold4(s2, hs);
+                *(f32x4 *)(ur + 4 * q) = times_g(hs, a.w2, 4 * q);
+            }
+        }
+    }
+    const double inv2 = block_inv_rms(s2, part, lane, wave, a.k, a.eps2);
+    if (v == 0) a.inv[(uint64_t)b * a.m + j] = inv2;
+}
+
 }  // namespace
+
+hipError_t launch_residual_rows(const ResidualArgs &a, uint32_t batch, hipStream_t s) {
+    ResidualArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel((const void *)residual_rows_kernel, dim3(batch * a.m), dim3(256), args, 0, s);
+}
 
 hipError_t launch_norm_rows(const NormArgs &a, uint32_t batch, hipStream_t s) {
     NormArgs copy = a;

@@ -36,7 +36,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = qfr.load_library()
     declared = _declared_functions()
-    assert len(declared) == 14, declared
+    assert len(declared) == 15, declared
     for name in declared:
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
@@ -370,3 +370,57 @@ def test_norm_work_bytes_is_the_header_formula():
     assert qfr.norm_work_bytes(256, 4, 1) == 4096 + 32
     assert qfr.norm_work_bytes(4, 1, 1) == 256 + 8
     assert qfr.norm_work_bytes(4096, 8, 16) == 16 * 8 * 4096 * 4 + 16 * 8 * 8
+
+
+C2, W2 = 0x7F7000000000, 0x7F8000000000
+
+
+def _resid(work=WK, work_bytes=1 << 20, **kw):
+    lib = qfr.load_library()
+    a = dict(h=RP, x=XP, w=GP, c=C2, w2=W2, eps=1e-5, eps2=1e-5, hout=HP, y=YP, W=WP, n=64, k=256, m=4,
+             wt=Weight.Q8_0)
+    a.update(kw)
+    rc = lib.row_exact_mv_residual_rmsnorm_ws(int(a["wt"]), a["W"], a["h"], a["x"], a["w"], a["c"], a["w2"], a["eps"],
+                                              a["eps2"], a["hout"], a["y"], a["n"], a["k"], a["m"], 1, None, work,
+                                              work_bytes, None)
+    return rc, qfr.row_exact_last_error()
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(h=0), -1, "h must be a non-NULL device pointer"),
+    (dict(eps=-1.0), -1, "eps and eps2 must be finite and >= 0"),
+    (dict(eps2=float("inf")), -1, "eps and eps2 must be finite and >= 0"),
+    (dict(eps2=float("nan")), -1, "eps and eps2 must be finite and >= 0"),
+    (dict(c=C2 + 4), -2, "h, w, c, w2 and hout must be 16-byte aligned"),
+    (dict(hout=HP + 8), -2, "16-byte aligned"),
+    (dict(w2=YP), -4, "y overlaps h, w, c or w2"),
+    (dict(h=YP + 64), -4, "y overlaps"),
+    (dict(hout=XP), -4, "hout overlaps"),
+    (dict(hout=RP + 16), -4, "hout overlaps"),          # part of h, not h itself
+    (dict(hout=GP), -4, "hout overlaps"),
+    (dict(work=0), -1, "work must be"),
+    (dict(work=WK + 8), -2, "work must sit on a 16-byte boundary"),
+    (dict(work_bytes=4 * 256 * 4), -1, "the call needs"),
+    (dict(work=HP), -4, "work overlaps"),
+    (dict(work=C2), -4, "work overlaps"),
+    (dict(x=0), -1, ""),
+    (dict(m=9), -1, "m = 9"),
+])
+def test_residual_rmsnorm_ws_invalid_arguments(kw, code, text):
+    before = qfr.row_exact_launch_count()
+    rc, msg = _resid(**kw)
+    assert rc == code, (rc, msg)
+    assert text in msg, msg
+    assert qfr.row_exact_launch_count() == before
+
+
+def test_residual_rmsnorm_ws_in_place_and_optional_vectors_pass_the_checks():
+    # hout == h (in place) and NULL w / c / w2 are valid; with no GPU the call
+    # then fails only at the launch, after every argument check (with a GPU
+    # these placeholder addresses would be launched on: not run there)
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("placeholder pointers: only where no GPU is visible")
+    for kw in (dict(hout=RP), dict(w=0, c=0, w2=0, hout=0)):
+        rc, msg = _resid(**kw)
+        assert rc == -7, (kw, rc, msg)

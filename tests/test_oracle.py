@@ -456,6 +456,45 @@ def test_gather_identity_and_selection():
     assert np.all(np.isnan(yg[1])) and not np.any(np.isnan(yg[[0, 2, 3]]))
 
 
+def test_residual_rmsnorm_reduces_and_normalises():
+    """With x = 0 the residual form is the add form (x := h, r := 0, g := w2,
+    eps := eps2) bit for bit; with h = 0, w = 1, no scaling and eps = 0 its
+    first normalisation alone has mean square 1 and is float32 x / rms in
+    float64; scaling x by 4 leaves it unchanged; the scaling c multiplies the
+    float32 sum after rounding; with w2 = 1, eps2 = 0 the second
+    normalisation has mean square 1; the product is a library float64 dot of
+    the dequantized weights with xn."""
+    t, n, k, m = wl.Q8_0, 5, 64, 3
+    W = wl.weights(t, n, k, seed=191)
+    h = wl.activations(m, k, seed=192)
+    x = wl.activations(m, k, seed=193)
+    w = (1.0 + wl.activations(1, k, seed=194)[0] * 0.1).astype(np.float32)
+    c = (0.5 + wl.activations(1, k, seed=195)[0] * 0.05).astype(np.float32)
+    w2 = (1.0 + wl.activations(1, k, seed=196)[0] * 0.1).astype(np.float32)
+    zero = np.zeros_like(x)
+    hs, xn, y, a = oracle.mv_residual_rmsnorm(t, W, h, zero, w, None, w2, 1e-3, 1e-5, n, k, m)
+    h2, xn2, y2, a2 = oracle.mv_add_rmsnorm(t, W, h, zero, w2, 1e-5, n, k, m)
+    assert np.array_equal(_bits32(hs), _bits32(h2)) and np.array_equal(xn, xn2)
+    assert np.array_equal(y, y2) and np.array_equal(a, a2)
+    # the first normalisation alone
+    hs, xn, _, _ = oracle.mv_residual_rmsnorm(t, W, zero, x, None, None, None, 0.0, 0.0, n, k, m)
+    x64 = x.astype(np.float64)
+    rms = np.sqrt((x64 ** 2).sum(axis=1, keepdims=True) / k)
+    assert np.max(np.abs(hs.reshape(m, k).astype(np.float64) - x64 / rms)) <= 2.0 ** -24 * 4
+    assert np.allclose((hs.reshape(m, k).astype(np.float64) ** 2).mean(axis=1), 1.0, rtol=1e-6)
+    hs4, _, _, _ = oracle.mv_residual_rmsnorm(t, W, zero, 4 * x, None, None, None, 0.0, 0.0, n, k, m)
+    assert np.array_equal(_bits32(hs4), _bits32(hs))
+    # the scaling acts on the rounded sum
+    hs_c, _, _, _ = oracle.mv_residual_rmsnorm(t, W, h, x, w, c, None, 1e-5, 1e-5, n, k, m)
+    hs_1, _, _, _ = oracle.mv_residual_rmsnorm(t, W, h, x, w, None, None, 1e-5, 1e-5, n, k, m)
+    assert np.array_equal(_bits32(hs_c), _bits32((hs_1.reshape(m, k) * c).ravel()))
+    # the second normalisation and the product
+    hs, xn, y, a = oracle.mv_residual_rmsnorm(t, W, h, x, w, c, None, 1e-5, 0.0, n, k, m)
+    assert np.allclose((xn[0] ** 2).mean(axis=1), 1.0, rtol=1e-14, atol=0)
+    wd = oracle.dequant(t, W, n, k).astype(np.float64)
+    assert np.all(np.abs(y[0] - xn[0] @ wd.T) <= 2 * k * 2.0 ** -53 * a[0])
+
+
 def test_add_rmsnorm_sum_and_normalisation():
     """h is numpy's float32 sum; with eps = 0 and g = 1 every normalised row
     has mean square 1; a constant row c normalises to c / sqrt(c^2 + eps);
