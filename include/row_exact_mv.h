@@ -240,8 +240,12 @@ int row_exact_mv_add_rmsnorm(row_exact_weight_t wt, const void *W, const float *
  *  work_bytes : its size.
  * Other arguments as row_exact_mv_add_rmsnorm.  Errors: as
  * row_exact_mv_add_rmsnorm, plus ROW_EXACT_EARG (NULL work, work_bytes too
- * small), ROW_EXACT_EALIGN and ROW_EXACT_EALIAS for work.  A launch error of
- * the second kernel leaves h written and y untouched. */
+ * small), ROW_EXACT_EALIGN and ROW_EXACT_EALIAS for work, and
+ * ROW_EXACT_EEXTENT when batch * m exceeds 2^31 - 1, when batch > 1 and
+ * m * k exceeds 2^32 - 1 (the work buffer's batch stride), or when the work
+ * buffer would span 2^62 bytes or more.  Both launches are planned before
+ * the first is enqueued: a call that fails its checks enqueues nothing.  A
+ * launch error of the second kernel leaves h written and y untouched. */
 int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *x, const float *r, const float *g,
                                 float eps, float *h, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                                 const row_exact_strides_t *strides, void *work, uint64_t work_bytes,
@@ -271,8 +275,10 @@ int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const floa
  *  work       : as row_exact_mv_add_rmsnorm_ws (ROW_EXACT_NORM_WORK_BYTES).
  * Other arguments as row_exact_mv.  Errors: as row_exact_mv, plus
  * ROW_EXACT_EARG (NULL h or work, eps or eps2 out of range, work_bytes too
- * small), ROW_EXACT_EALIGN, and ROW_EXACT_EALIAS (y against h, w, c, w2;
- * hout against everything but h; work against every operand). */
+ * small), ROW_EXACT_EALIGN, ROW_EXACT_EALIAS (y against h, w, c, w2; hout
+ * against everything but h; work against every operand) and
+ * ROW_EXACT_EEXTENT as row_exact_mv_add_rmsnorm_ws.  A call that fails its
+ * checks enqueues nothing (hout untouched). */
 int row_exact_mv_residual_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *h, const float *x,
                                      const float *w, const float *c, const float *w2, float eps, float eps2,
                                      float *hout, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,

@@ -586,22 +586,23 @@ int run_norm_two_launch(int t, const void *W, const float *x, float *y, uint32_t
                         uint32_t batch, const row_exact_strides_t &s, const Norm &nm, hipStream_t stream,
                         void *work);
 
-// row_scale: per (batch entry, input row) output scales, [batch][m] (the
-// second launch of the two-launch fused normalisation), or NULL.
-int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
-        const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream,
-        const int32_t *ids = nullptr, uint32_t num_experts = 0, const Norm *norm = nullptr,
-        const double *row_scale = nullptr, void *norm_work = nullptr) {
-    g_err.clear();
-    const row_exact_strides_t s = resolve_strides(strides, m, n, k);
-    uint64_t wb, xbytes, ybytes;
-    int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes, ids, num_experts);
-    if (rc) return rc;
-    if (norm) {
-        rc = validate_norm(*norm, W, x, y, k, wb, xbytes, ybytes);
-        if (rc) return rc;
-        if (norm_work) return run_norm_two_launch(t, W, x, y, n, k, m, batch, s, *norm, stream, norm_work);
-    }
+// A product launch, scheduled and checked, not yet enqueued.
+struct MvLaunch {
+    int t;
+    MvArgs a;
+    uint32_t m, nr;
+    dim3 grid, block;
+    size_t lds, lds_max;
+};
+
+// Schedules the product of operands that have passed validate_mv (strides
+// resolved) and fills its launch; enqueues nothing.  row_scale: per (batch
+// entry, input row) output scales, [batch][m] (the second launch of the
+// two-launch normalisations), or NULL.
+int plan_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+            const row_exact_strides_t &s, const row_exact_schedule_t *pin, const int32_t *ids, uint32_t num_experts,
+            const Norm *norm, const double *row_scale, MvLaunch &L) {
+    int rc = 0;
     if (pin) {
         rc = check_schedule_fields(t, k, *pin);
         if (rc) return rc;
@@ -686,12 +687,44 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
     const uint64_t grid_x = (uint64_t)wgs * batch;
     if (grid_x > 0x7fffffffull)
         return fail(ROW_EXACT_ESCHEDULE, "grid of %llu workgroups exceeds the launch limit", (unsigned long long)grid_x);
-    const size_t lds = lds_bytes(t, m, k, sch.k_chunk, sch.k_split);
-    hipError_t e =
-        mv_launcher(t)(a, m, nr, dim3((uint32_t)grid_x), dim3(64 * sch.waves_per_workgroup), lds, di.lds_max, stream);
+    L.t = t;
+    L.a = a;
+    L.m = m;
+    L.nr = nr;
+    L.grid = dim3((uint32_t)grid_x);
+    L.block = dim3(64 * sch.waves_per_workgroup);
+    L.lds = lds_bytes(t, m, k, sch.k_chunk, sch.k_split);
+    L.lds_max = di.lds_max;
+    return 0;
+}
+
+int enqueue_mv(const MvLaunch &L, hipStream_t stream) {
+    hipError_t e = mv_launcher(L.t)(L.a, L.m, L.nr, L.grid, L.block, L.lds, L.lds_max, stream);
     if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     g_launches.fetch_add(1, std::memory_order_relaxed);
     return 0;
+}
+
+// Validates every operand, then plans and enqueues the product (two launches
+// for the fused normalisation on a work buffer).
+int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
+        const row_exact_strides_t *strides, const row_exact_schedule_t *pin, hipStream_t stream,
+        const int32_t *ids = nullptr, uint32_t num_experts = 0, const Norm *norm = nullptr,
+        void *norm_work = nullptr) {
+    g_err.clear();
+    const row_exact_strides_t s = resolve_strides(strides, m, n, k);
+    uint64_t wb, xbytes, ybytes;
+    int rc = validate_mv(t, W, x, y, n, k, m, batch, s, wb, xbytes, ybytes, ids, num_experts);
+    if (rc) return rc;
+    if (norm) {
+        rc = validate_norm(*norm, W, x, y, k, wb, xbytes, ybytes);
+        if (rc) return rc;
+        if (norm_work) return run_norm_two_launch(t, W, x, y, n, k, m, batch, s, *norm, stream, norm_work);
+    }
+    MvLaunch L;
+    rc = plan_mv(t, W, x, y, n, k, m, batch, s, pin, ids, num_experts, norm, nullptr, L);
+    if (rc) return rc;
+    return enqueue_mv(L, stream);
 }
 
 // Bytes of the two-launch fused normalisation's work buffer: u ([batch][m][k]
@@ -700,6 +733,37 @@ int run(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t k, 
 uint64_t norm_work_bytes(uint32_t k, uint32_t m, uint32_t batch) {
     const uint64_t u = ((uint64_t)batch * m * k * sizeof(float) + 255) & ~255ull;
     return u + (uint64_t)batch * m * sizeof(double);
+}
+
+// The product of the two-launch normalisations on the work buffer: u =
+// [batch][m][k] floats, each output scaled by its row's inv ([batch][m]
+// doubles), y in the caller's layout s.  Planned before the first of the two
+// launches, so that a call that fails enqueues nothing.  Also checks the
+// extents the work buffer's layout adds (the u view's batch stride m * k and
+// the first launch's grid of batch * m workgroups); the caller has checked
+// W, y and the work buffer itself.
+int plan_scaled_product(int t, const void *W, const float *u, float *y, uint32_t n, uint32_t k, uint32_t m,
+                        uint32_t batch, const row_exact_strides_t &s, const double *inv, MvLaunch &L) {
+    if ((uint64_t)batch * m > 0x7fffffffull)
+        return fail(ROW_EXACT_EEXTENT, "batch (%u) x m (%u) normalised rows exceed one launch's 2^31 - 1 workgroups",
+                    batch, m);
+    if (batch > 1 && (uint64_t)m * k > 0xffffffffull)
+        return fail(ROW_EXACT_EEXTENT, "m (%u) x k (%u) values per batch entry exceed the 32-bit batch stride", m, k);
+    row_exact_strides_t su;
+    su.x_row_stride = k;
+    su.x_batch_stride = batch > 1 ? m * k : 0;
+    su.y_row_stride = s.y_row_stride;
+    su.y_batch_stride = s.y_batch_stride;
+    return plan_mv(t, W, u, y, n, k, m, batch, su, nullptr, nullptr, 0, nullptr, inv, L);
+}
+
+// Work bytes of a call, or 0 (with the error set) when they reach 2^62.
+uint64_t checked_norm_work_bytes(uint32_t k, uint32_t m, uint32_t batch) {
+    if ((unsigned __int128)batch * m * k * sizeof(float) >= ((unsigned __int128)1 << 62)) {
+        fail(ROW_EXACT_EEXTENT, "the work buffer of batch %u x m %u x k %u floats spans 2^62 bytes or more", batch, m, k);
+        return 0;
+    }
+    return norm_work_bytes(k, m, batch);
 }
 
 // Scratch of row_exact_mv_add_rmsnorm_noalloc (the work buffer of the
@@ -753,20 +817,13 @@ int run_norm_two_launch(int t, const void *W, const float *x, float *y, uint32_t
     na.k = k;
     na.m = m;
     na.eps = nm.eps;
-    int rc = 0;
+    MvLaunch L;
+    int rc = plan_scaled_product(t, W, u, y, n, k, m, batch, s, inv, L);
+    if (rc) return rc;
     hipError_t e = launch_norm_rows(na, batch, stream);
-    if (e != hipSuccess) {
-        rc = fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-    } else {
-        g_launches.fetch_add(1, std::memory_order_relaxed);
-        row_exact_strides_t su;
-        su.x_row_stride = k;
-        su.x_batch_stride = m * k;
-        su.y_row_stride = s.y_row_stride;
-        su.y_batch_stride = s.y_batch_stride;
-        rc = run(t, W, u, y, n, k, m, batch, &su, nullptr, stream, nullptr, 0, nullptr, inv);
-    }
-    return rc;
+    if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    return enqueue_mv(L, stream);
 }
 
 }  // namespace
@@ -814,7 +871,8 @@ int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const floa
     if (rc) return rc;
     if (!work) return fail(ROW_EXACT_EARG, "work must be a non-NULL device pointer");
     if ((uintptr_t)work % 16) return fail(ROW_EXACT_EALIGN, "work must sit on a 16-byte boundary");
-    const uint64_t need = norm_work_bytes(k, m, batch);
+    const uint64_t need = checked_norm_work_bytes(k, m, batch);
+    if (!need) return ROW_EXACT_EEXTENT;
     if (work_bytes < need)
         return fail(ROW_EXACT_EARG, "work holds %llu bytes, the call needs %llu", (unsigned long long)work_bytes,
                     (unsigned long long)need);
@@ -829,7 +887,7 @@ int row_exact_mv_add_rmsnorm_ws(row_exact_weight_t wt, const void *W, const floa
         (h && overlap(wp, need, (uintptr_t)h, xb)) || (g && overlap(wp, need, (uintptr_t)g, 4ull * k)))
         return fail(ROW_EXACT_EALIAS, "work overlaps W, x, r, g, h or y");
     const Norm nm{r, g, h, eps};
-    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, nullptr, work);
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, work);
 }
 
 int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const float *x, const float *r,
@@ -838,7 +896,8 @@ int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const
     g_err.clear();
     int rc = check_shape((int)wt, n, k, m, batch);
     if (rc) return rc;
-    const uint64_t need = norm_work_bytes(k, m, batch);
+    const uint64_t need = checked_norm_work_bytes(k, m, batch);
+    if (!need) return ROW_EXACT_EEXTENT;
     if (need > ROW_EXACT_NOALLOC_SCRATCH_BYTES)
         return fail(ROW_EXACT_EEXTENT,
                     "the call needs %llu bytes of scratch (ROW_EXACT_NORM_WORK_BYTES), the allocation-free "
@@ -848,7 +907,7 @@ int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const
     rc = noalloc_scratch(ptr);
     if (rc) return rc;
     const Norm nm{r, g, h, eps};
-    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, nullptr, ptr);
+    return run((int)wt, W, x, y, n, k, m, batch, strides, nullptr, stream, nullptr, 0, &nm, ptr);
 }
 
 int row_exact_mv_residual_rmsnorm_ws(row_exact_weight_t wt, const void *W, const float *h, const float *x,
@@ -883,7 +942,8 @@ int row_exact_mv_residual_rmsnorm_ws(row_exact_weight_t wt, const void *W, const
     }
     if (!work) return fail(ROW_EXACT_EARG, "work must be a non-NULL device pointer");
     if ((uintptr_t)work % 16) return fail(ROW_EXACT_EALIGN, "work must sit on a 16-byte boundary");
-    const uint64_t need = norm_work_bytes(k, m, batch);
+    const uint64_t need = checked_norm_work_bytes(k, m, batch);
+    if (!need) return ROW_EXACT_EEXTENT;
     if (work_bytes < need)
         return fail(ROW_EXACT_EARG, "work holds %llu bytes, the call needs %llu", (unsigned long long)work_bytes,
                     (unsigned long long)need);
@@ -908,15 +968,13 @@ int row_exact_mv_residual_rmsnorm_ws(row_exact_weight_t wt, const void *W, const
     ra.m = m;
     ra.eps = eps;
     ra.eps2 = eps2;
+    MvLaunch L;
+    rc = plan_scaled_product((int)wt, W, ra.u, y, n, k, m, batch, s, ra.inv, L);
+    if (rc) return rc;
     hipError_t e = launch_residual_rows(ra, batch, stream);
     if (e != hipSuccess) return fail(ROW_EXACT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     g_launches.fetch_add(1, std::memory_order_relaxed);
-    row_exact_strides_t su;
-    su.x_row_stride = k;
-    su.x_batch_stride = m * k;
-    su.y_row_stride = s.y_row_stride;
-    su.y_batch_stride = s.y_batch_stride;
-    return run((int)wt, W, ra.u, y, n, k, m, batch, &su, nullptr, stream, nullptr, 0, nullptr, ra.inv);
+    return enqueue_mv(L, stream);
 }
 
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,

@@ -337,12 +337,13 @@ def test_add_rmsnorm_invalid_arguments(kw, code, text):
 WK = 0x7F6000000000
 
 
-def _norm_ws(work=WK, work_bytes=1 << 20, **kw):
+def _norm_ws(work=WK, work_bytes=1 << 20, batch=1, strides=None, **kw):
     lib = qfr.load_library()
     a = dict(r=RP, g=GP, h=HP, eps=1e-5, x=XP, y=YP, W=WP, n=64, k=256, m=4, wt=Weight.Q8_0)
     a.update(kw)
+    sp = ctypes.byref(strides) if strides is not None else None
     rc = lib.row_exact_mv_add_rmsnorm_ws(int(a["wt"]), a["W"], a["x"], a["r"], a["g"], a["eps"], a["h"], a["y"], a["n"],
-                                         a["k"], a["m"], 1, None, work, work_bytes, None)
+                                         a["k"], a["m"], batch, sp, work, work_bytes, None)
     return rc, qfr.row_exact_last_error()
 
 
@@ -375,13 +376,14 @@ def test_norm_work_bytes_is_the_header_formula():
 C2, W2 = 0x7F7000000000, 0x7F8000000000
 
 
-def _resid(work=WK, work_bytes=1 << 20, **kw):
+def _resid(work=WK, work_bytes=1 << 20, batch=1, strides=None, **kw):
     lib = qfr.load_library()
     a = dict(h=RP, x=XP, w=GP, c=C2, w2=W2, eps=1e-5, eps2=1e-5, hout=HP, y=YP, W=WP, n=64, k=256, m=4,
              wt=Weight.Q8_0)
     a.update(kw)
+    sp = ctypes.byref(strides) if strides is not None else None
     rc = lib.row_exact_mv_residual_rmsnorm_ws(int(a["wt"]), a["W"], a["h"], a["x"], a["w"], a["c"], a["w2"], a["eps"],
-                                              a["eps2"], a["hout"], a["y"], a["n"], a["k"], a["m"], 1, None, work,
+                                              a["eps2"], a["hout"], a["y"], a["n"], a["k"], a["m"], batch, sp, work,
                                               work_bytes, None)
     return rc, qfr.row_exact_last_error()
 
@@ -424,3 +426,34 @@ def test_residual_rmsnorm_ws_in_place_and_optional_vectors_pass_the_checks():
     for kw in (dict(hout=RP), dict(w=0, c=0, w2=0, hout=0)):
         rc, msg = _resid(**kw)
         assert rc == -7, (kw, rc, msg)
+
+
+# Extents that only the work buffer's layout adds: the normalisation's grid
+# of batch x m workgroups, the u view's batch stride m x k (32 bits), and the
+# work size itself.  Each call is refused before the first of its two
+# launches (x broadcast over the batch keeps the operands' own extents small).
+_M8_BIG_BATCH = dict(n=1, k=32, m=8, batch=(1 << 28) + 1, strides=Strides(32, 0, 1, 8), work_bytes=1 << 40)
+_M8_LONG_ROWS = dict(n=1, k=1 << 29, m=8, batch=2, strides=Strides(1 << 29, 0, 1, 8), work_bytes=1 << 36)
+
+
+@pytest.mark.parametrize("case,text", [
+    (_M8_BIG_BATCH, "normalised rows exceed one launch"),
+    (_M8_LONG_ROWS, "exceed the 32-bit batch stride"),
+])
+def test_two_launch_norm_extents_refused_before_any_launch(case, text):
+    before = qfr.row_exact_launch_count()
+    rc, msg = _norm_ws(**case)
+    assert rc == -5 and text in msg, (rc, msg)
+    rc, msg = _resid(w=0, c=0, w2=0, **case)
+    assert rc == -5 and text in msg, (rc, msg)
+    assert qfr.row_exact_launch_count() == before
+
+
+def test_work_size_overflow_refused():
+    # batch x m x k floats of 2^62 bytes or more: refused, not wrapped to a
+    # small size that a small buffer would satisfy
+    s = Strides(1 << 30, 0, 1, 8)
+    for f in (_norm_ws, _resid):
+        # W (2^28 sets of one 1.1 GB row) placed above every other operand
+        rc, msg = f(W=1 << 63, n=1, k=1 << 30, m=8, batch=1 << 28, strides=s, work_bytes=(1 << 64) - 1)
+        assert rc == -5 and "spans 2^62 bytes" in msg, (rc, msg)
