@@ -21,6 +21,10 @@
 #ifndef REX_WALK_UNCONDITIONAL_MIN_ITEMS
 #define REX_WALK_UNCONDITIONAL_MIN_ITEMS 3
 #endif
+// 1: rows of 64 s + 32 pieces take 32 lanes per row (see lane_map_log2).
+#ifndef REX_HALF_STEP_LANES
+#define REX_HALF_STEP_LANES 1
+#endif
 
 using namespace rex;
 
@@ -277,6 +281,28 @@ uint32_t derived_k_split(int t, uint32_t k, uint32_t rows) {
     return K;
 }
 
+// Lanes per row (log2) of the product under reduction split K: 16 or 32
+// for rows of at most 16 / 32 pieces; 32 also for unsplit rows of the
+// block-quantized types whose pieces leave the last 64-lane wave step
+// exactly half empty (64 s + 32 pieces, e.g. Q6_K k = 14336: 3.5 steps of
+// 64 lanes), which then take 2 s + 1 whole 32-lane steps with two rows per
+// wave; 64 otherwise.  Measured on MI355X at n = 4096, 1.5 and 3.5 steps,
+// m = 1..8: Q4_K, Q6_K and Q5_0 4-28% faster (Q6_K 4096 x 14336 at m = 1:
+// -10%), Q8_0 -4% to -10% except +8% at 1.5 steps and m = 1; the dense
+// types, whose pieces carry little vector work per byte, 4-18% slower (half
+// as many waves for the same rows).  Part of the numerics (the lane
+// partials and their tree), so a function of (type, k, K) only.  A lane
+// addresses the rows of its slot by a 32-bit offset from the wave's first
+// row (up to 4 rows per slot), so the map is kept to rows under 2^29 bytes.
+uint32_t lane_map_log2(int t, uint32_t k, uint32_t K) {
+    const uint32_t lpr = lanes_per_row_log2(t, k);
+    const bool blocks = t == kQ8_0 || t == kQ4K || t == kQ6K || t == kQ5_0;
+    if (REX_HALF_STEP_LANES && blocks && lpr == 6 && K == 1 && pieces_of(t, k) % 64 == 32 &&
+        row_bytes_of(t, k) < (1u << 29))
+        return 5;
+    return lpr;
+}
+
 MvAttributes mv_attributes(int t) {
     switch (t) {
     case kF16: return attributes_mv_f16;
@@ -413,7 +439,7 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         // single rows on 24 waves per CU instead, so each wave walks two or
         // more of them (Q4_K 14336 x 4096: 12.3 -> 10.8 us at m = 1).
         uint64_t target = (uint64_t)di.cus * 32;
-        const uint32_t lpr = lanes_per_row_log2(t, k);
+        const uint32_t lpr = lane_map_log2(t, k, 1);
         const uint64_t wave_rows = rows >> (6 - lpr);  // rows / slots per wave
         const uint32_t steps = (pieces_of(t, k) + (1u << lpr) - 1) >> lpr;
         uint32_t nr = 1;
@@ -430,7 +456,7 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
             }
         }
         s.rows_per_wave = nr;
-        const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
+        const uint32_t rg = nr << (6 - lpr);  // rows per group
         const uint32_t gpb = (n + rg - 1) / rg;
         const uint32_t waves = waves_per_workgroup(gpb, batch, di.cus, m, kc);
         s.waves_per_workgroup = waves;
@@ -447,12 +473,18 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         s.workgroups_per_batch = (uint32_t)(w < max_wgs ? w : max_wgs);
         return 0;
     }
-    // rows per wave: the most that still leaves 8 waves per CU
+    // rows per wave: the most that still leaves 8 waves per CU.  Q6_K rows
+    // on 32 lanes (two row slots per wave) in several LDS passes count as on
+    // 64 from m = 7, so each x value read from LDS feeds two rows per slot
+    // (4096 x 14336 at m = 8: -5%; at m = 5, 6 and for Q4_K and Q8_0 rows of
+    // 3.5 steps at m = 5 and 8, one row per slot is 4-16% faster)
     const uint64_t target_waves = (uint64_t)di.cus * 8;
-    const uint32_t lpr = lanes_per_row_log2(t, k);
+    const uint32_t lpr = lane_map_log2(t, k, 1);
     const uint64_t wave_rows = rows >> (6 - lpr);
+    const bool long_sub = lpr < 6 && pieces_of(t, k) > 32;
+    const uint64_t nr_rows = (long_sub && t == kQ6K && m >= 7 && kc < k) ? rows : wave_rows;
     uint32_t nr = max_rows_per_wave(t, m);
-    while (nr > 1 && wave_rows / nr < target_waves) nr >>= 1;
+    while (nr > 1 && nr_rows / nr < target_waves) nr >>= 1;
     // Up to 4 input rows and fewer than 16 rows per wave: single rows for
     // rows of several wave steps, so each wave walks more items with loads
     // in flight behind the multiply (3-10% faster than 2 or 4 rows per wave
@@ -462,11 +494,11 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     // 128256-row head keeps 4.  Short rows (a wave already covers 2 or 4
     // rows per item) and the fused-norm instances measured slower with it
     // and keep the rule above.
-    const uint32_t steps = (pieces_of(t, k) + 63) >> 6;
-    if (m <= 4 && kc >= k && lpr == 6 && !fused_norm && wave_rows < 16 * target_waves)
+    const uint32_t steps = (pieces_of(t, k) + (1u << lpr) - 1) >> lpr;
+    if (m <= 4 && kc >= k && (lpr == 6 || steps >= 2) && !fused_norm && wave_rows < 16 * target_waves)
         nr = steps >= 2 ? 1u : (nr < 2u ? nr : 2u);  // never more than leaves 8 waves per CU
     s.rows_per_wave = nr;
-    const uint32_t rg = nr << (6 - lanes_per_row_log2(t, k));  // rows per group
+    const uint32_t rg = nr << (6 - lpr);  // rows per group
     const uint32_t gpb = (n + rg - 1) / rg;
     const uint32_t waves = waves_per_workgroup(gpb, batch, di.cus, m, kc);
     s.waves_per_workgroup = waves;
@@ -634,7 +666,7 @@ int plan_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t
     a.xrs = s.x_row_stride;
     a.yrs = s.y_row_stride;
     a.pieces = pieces_of(t, k);
-    a.lpr_log2 = lanes_per_row_log2(t, k);
+    a.lpr_log2 = lane_map_log2(t, k, sch.k_split);
     const uint32_t nr = sch.rows_per_wave;
     const uint32_t rg = nr << (6 - a.lpr_log2);  // rows per group: NR rows in each of the wave's slots
     a.groups_per_batch = (n + rg - 1) / rg;

@@ -7,9 +7,12 @@
 //   - A weight row is cut into "pieces": per-lane work items whose bytes sit
 //     together in the row (F16: 8 values; Q8_0 / Q5_0: one block; Q4_K: 32
 //     nibble bytes, two sub-blocks, of a super-block; Q6_K: a quarter
-//     super-block).  Lane L of the wave owning the row takes pieces L, L+64,
-//     L+128, ... in that order, so each load instruction of a wave covers
-//     adjacent bytes of the row.
+//     super-block).  A row has 64 lanes of a wave, or 32 / 16 (two / four
+//     rows per wave) for rows of at most 32 / 16 pieces and, for the
+//     block-quantized types, rows whose pieces would leave the last 64-lane
+//     step half empty.  Lane L of the row's L_row lanes takes pieces L,
+//     L + L_row, L + 2 L_row, ... in that order, so each load instruction of
+//     a wave covers adjacent bytes of each of its rows.
 //   - A wave streams rows_per_wave (NR) rows at once: every input value read
 //     from LDS feeds all NR weight rows (the page's nr0 packing).
 //   - The m input rows of the batch are staged once per pass into LDS
@@ -32,7 +35,8 @@
 //     packing (NR, waves per workgroup, grid).
 //   - The 64 lane partials of an output are added by one fixed tree: lanes
 //     (L, L^32), then (L, L^16), then within each row of 16 lanes: rotate-8,
-//     half-row mirror, xor 2, xor 1.  The first two levels are done with the
+//     half-row mirror, xor 2, xor 1 (rows on 32 or 16 lanes: the same tree
+//     without its first one or two levels).  The first two levels are done with the
 //     gfx950 permlane32/permlane16 swaps and, when a lane holds several
 //     outputs, transposed (each swap hands half of the outputs to the other
 //     half of the wave, so no work is duplicated); the rest with DPP.  IEEE
@@ -1074,9 +1078,10 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
     }
 }
 
-// Pieces pb + lane, pb + lane + stride, ... below pe of the NR rows (stride
-// 64, or 64 K for the K-split, whose wave ws starts at pb + 64 ws), with the
-// next piece's loads issued before the current piece's math.
+// Pieces pb + lane, pb + lane + stride, ... below pe of the NR rows (lane:
+// the lane's index in its row slot; stride: the lanes per row, or 64 K for
+// the K-split, whose wave ws starts at pb + 64 ws), with the next piece's
+// loads issued before the current piece's math.
 template <int T, int M, int NR>
 __device__ __forceinline__ void accumulate(float (&acc)[NR][M], const uint8_t *const (&R)[NR],
                                            const uint32_t (&o0)[NR], uint32_t pb, uint32_t pe, uint32_t vb,
@@ -1302,7 +1307,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
         // x by LDS DMA ahead of the first items' weights (types whose pieces
         // take a fixed number of load instructions), chosen by the host where
         // x exceeds what the register staging requests ahead (a.x_dma)
-        constexpr bool DMA = !NORM && !SUB && REX_X_DMA && Tr<T>::LOADS > 0 && M == 1;
+        constexpr bool DMA = !NORM && REX_X_DMA && Tr<T>::LOADS > 0 && M == 1;
         constexpr bool UP = UNC || XF || DMA;
         auto prefetch_first = [&] {
             fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, A);
@@ -1364,14 +1369,18 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 }
             }
         }
-    } else if constexpr (!SUB) {
-        // Several LDS passes over K, or a K split (both only for rows of
-        // more than 64 pieces, so 64 lanes per row): every K waves of the
-        // workgroup work on one row group per round (wave ws of the K takes
-        // the row's wave steps ws, ws + K, ws + 2K, ..., in that order
-        // across the passes, so a pass of fewer than K steps leaves some of
-        // the K waves without work) and all waves stage each pass together.
-        const uint32_t K = a.k_split;
+    } else {
+        // Several LDS passes over K, or a K split (64 lanes per row only):
+        // every K waves of the workgroup work on one row group per round
+        // (wave ws of the K takes the row's wave steps ws, ws + K, ws + 2K,
+        // ..., in that order across the passes, so a pass of fewer than K
+        // steps leaves some of the K waves without work) and all waves stage
+        // each pass together.  With L < 64 lanes per row (no split) a lane
+        // takes pieces li, li + L, ... of the row in its slot, in the order
+        // of the single pass.
+        const uint32_t K = SUB ? 1u : a.k_split;
+        const uint32_t lpr = lpr_of<SUB>(a);
+        const uint32_t li = lane & ((1u << lpr) - 1), slot = lane >> lpr;
         const uint32_t slots = nwaves / K;               // row groups per round
         const uint32_t gs = wave / K, ws = wave - gs * K;  // group slot, split index
         float *kp = (float *)((uint8_t *)xs + a.kp_offset);
@@ -1389,7 +1398,7 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             zero<M, NR>(acc);
             const uint8_t *R[NR];
             uint32_t o0[NR];
-            row_bases<NR>(a.W, Wb, a.row_bytes, a.n, g * NR, false, 0, R, o0);
+            row_bases<NR>(a.W, Wb, a.row_bytes, a.n, (g * NR) << (6 - lpr), SUB, slot * NR, R, o0);
             for (uint32_t c = 0; c < a.nchunks; ++c) {
                 const uint32_t pb = c * a.pieces_per_chunk;
                 const uint32_t pe = min(pb + a.pieces_per_chunk, a.pieces);
@@ -1410,10 +1419,12 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
                 const uint32_t s0 = pb >> 6;
                 const uint32_t first = s0 + ((ws - s0) & (K - 1));
                 if (active)
-                    accumulate<T, M, NR>(acc, R, o0, 64 * first, pe, vb, xs, XS, a.k, lane,
-                                         (const float *)((const uint8_t *)xs + a.sx_offset), a.sx_stride, 64 * K);
+                    accumulate<T, M, NR>(acc, R, o0, 64 * first, pe, vb, xs, XS, a.k, li,
+                                         (const float *)((const uint8_t *)xs + a.sx_offset), a.sx_stride, K << lpr);
             }
-            if (K == 1) {
+            if constexpr (SUB) {
+                if (active) store_group<M, NR, true>(a, acc, yb, g, lane, sc);
+            } else if (K == 1) {
                 if (active) reduce_store<M, NR, 64>(acc, yb, a.yrs, a.n, g * NR, lane, sc);
             } else {
                 reduce_store_split<M, NR>(acc, kp, K, wave, ws, active, yb, a.yrs, a.n, g * NR, lane, sc);
@@ -1480,11 +1491,14 @@ hipError_t launch_instance(const MvArgs &a, dim3 grid, dim3 block, size_t lds, s
 
 template <int T, int M, int NR>
 hipError_t launch_one(const MvArgs &a, dim3 grid, dim3 block, size_t lds, size_t lds_max, hipStream_t s) {
-    // Unconditional-load walks (see fetch_item) only for the plain 64-lane
-    // instances, where waves hold many items on the large shapes.
-    if (a.lpr_log2 < 6)
-        return a.r ? launch_instance<T, M, NR, true, true, false>(a, grid, block, lds, lds_max, s)
-                   : launch_instance<T, M, NR, true, false, false>(a, grid, block, lds, lds_max, s);
+    // Unconditional-load walks (see fetch_item) only for the plain
+    // (unnormalised) instances, where waves hold many items on the large
+    // shapes.
+    if (a.lpr_log2 < 6) {
+        if (a.r) return launch_instance<T, M, NR, true, true, false>(a, grid, block, lds, lds_max, s);
+        if (a.walk_unconditional) return launch_instance<T, M, NR, true, false, true>(a, grid, block, lds, lds_max, s);
+        return launch_instance<T, M, NR, true, false, false>(a, grid, block, lds, lds_max, s);
+    }
     if (a.r) return launch_instance<T, M, NR, false, true, false>(a, grid, block, lds, lds_max, s);
     if (a.walk_unconditional) return launch_instance<T, M, NR, false, false, true>(a, grid, block, lds, lds_max, s);
     return launch_instance<T, M, NR, false, false, false>(a, grid, block, lds, lds_max, s);
