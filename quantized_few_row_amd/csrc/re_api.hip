@@ -21,7 +21,8 @@
 #ifndef REX_WALK_UNCONDITIONAL_MIN_ITEMS
 #define REX_WALK_UNCONDITIONAL_MIN_ITEMS 3
 #endif
-// 1: rows of 64 s + 32 pieces take 32 lanes per row (see lane_map_log2).
+// 1: rows whose last 64-lane step is at most half full take 32 lanes per
+// row (see lane_map_log2).
 #ifndef REX_HALF_STEP_LANES
 #define REX_HALF_STEP_LANES 1
 #endif
@@ -283,21 +284,25 @@ uint32_t derived_k_split(int t, uint32_t k, uint32_t rows) {
 
 // Lanes per row (log2) of the product under reduction split K: 16 or 32
 // for rows of at most 16 / 32 pieces; 32 also for unsplit rows of the
-// block-quantized types whose pieces leave the last 64-lane wave step
-// exactly half empty (64 s + 32 pieces, e.g. Q6_K k = 14336: 3.5 steps of
-// 64 lanes), which then take 2 s + 1 whole 32-lane steps with two rows per
-// wave; 64 otherwise.  Measured on MI355X at n = 4096, 1.5 and 3.5 steps,
-// m = 1..8: Q4_K, Q6_K and Q5_0 4-28% faster (Q6_K 4096 x 14336 at m = 1:
-// -10%), Q8_0 -4% to -10% except +8% at 1.5 steps and m = 1; the dense
-// types, whose pieces carry little vector work per byte, 4-18% slower (half
-// as many waves for the same rows).  Part of the numerics (the lane
+// block-quantized types whose last 64-lane wave step would be at most half
+// full (64 s + r pieces, 0 < r <= 32; e.g. Q6_K k = 14336: 3.5 steps of 64
+// lanes): on 32 lanes, two rows per wave, such a row issues half a 64-lane
+// step less; 64 otherwise.  Measured on MI355X, interleaved against 64
+// lanes, n = 4096 (Q5_0: 16 x 1024 grouped), m = 1, 2, 4, 8: Q6_K
+// 4096 x 14336 -9% at m = 1 and -2% to -8% above; rows of 1.5, 3.5 and
+// 5.4 steps of Q4_K, Q6_K, Q5_0 and Q8_0 -4% to -28% with few exceptions;
+// rows of about one step (Q8_0 k = 2112 and 3072, Q4_K k = 4352) +4% to +8%
+// at m = 1 and 2, -4% to -14% above; the dense types, whose pieces carry
+// little vector work per byte, 4-18% slower (half as many waves for the
+// same rows), so they keep 64 lanes.  Part of the numerics (the lane
 // partials and their tree), so a function of (type, k, K) only.  A lane
 // addresses the rows of its slot by a 32-bit offset from the wave's first
 // row (up to 4 rows per slot), so the map is kept to rows under 2^29 bytes.
 uint32_t lane_map_log2(int t, uint32_t k, uint32_t K) {
     const uint32_t lpr = lanes_per_row_log2(t, k);
     const bool blocks = t == kQ8_0 || t == kQ4K || t == kQ6K || t == kQ5_0;
-    if (REX_HALF_STEP_LANES && blocks && lpr == 6 && K == 1 && pieces_of(t, k) % 64 == 32 &&
+    const uint32_t tail = pieces_of(t, k) % 64;
+    if (REX_HALF_STEP_LANES && blocks && lpr == 6 && K == 1 && tail > 0 && tail <= 32 &&
         row_bytes_of(t, k) < (1u << 29))
         return 5;
     return lpr;

@@ -1,10 +1,11 @@
-"""Rows whose pieces leave the last 64-lane wave step half empty.
+"""Rows whose last 64-lane wave step would be at most half full.
 
-A row of 64 s + 32 pieces (Q6_K k = 14336: 224 pieces, 3.5 steps of 64
-lanes) takes 32 lanes per row instead, two rows per wave, 2 s + 1 whole
-steps, unless the reduction is split across waves (the split keeps 64
-lanes).  The lane map is part of the numerics and follows from (type, k,
-split) alone.  Checked here for every weight type at 1.5 and 3.5 steps:
+A row of 64 s + r pieces, 0 < r <= 32 (Q6_K k = 14336: 224 pieces, 3.5
+steps of 64 lanes), of a block-quantized type takes 32 lanes per row
+instead, two rows per wave, unless the reduction is split across waves (the
+split keeps 64 lanes); the dense types keep 64 lanes.  The lane map is part
+of the numerics and follows from (type, k, split) alone.  Checked here for
+every weight type at 66, 96, 130 and 224 pieces (tails of 2 and 32):
   - every output within the tolerance of the float64 oracle at every m, each
     row bitwise equal to its m = 1 result, repeats bitwise equal;
   - packing inert: rows per wave, waves, workgroups and LDS passes (one and
@@ -31,28 +32,35 @@ pytestmark = pytest.mark.gpu
 STEP = {wl.F16: 512, wl.Q8_0: 2048, wl.Q4_K: 4096, wl.Q6_K: 4096, wl.Q5_0: 2048, wl.F32: 256, wl.BF16: 512}
 TYPES = list(STEP)
 IDS = [wl.TYPE_NAMES[t] for t in TYPES]
-HALVES = (3, 7)  # k = 1.5 and 3.5 wave steps
+# 64 s + r pieces, r = 2 (4 where a piece is a quarter of a 256-value
+# super-block, so that k stays whole super-blocks) or 32
+PIECES = ("short_tail_1", 96, "short_tail_2", 224)
 N = 600  # enough rows that the derived split is 1 (a split keeps 64 lanes)
 
 
-def _k(t, halves):
-    return STEP[t] * halves // 2
+def _pieces(t, p):
+    r = 4 if t in (wl.Q4_K, wl.Q6_K) else 2
+    return {"short_tail_1": 64 + r, "short_tail_2": 128 + r}.get(p, p)
+
+
+def _k(t, p):
+    return STEP[t] // 64 * _pieces(t, p)
 
 
 @pytest.fixture(scope="module")
 def data():
     out = {}
     for t in TYPES:
-        for h in HALVES:
+        for h in PIECES:
             k = _k(t, h)
-            W = wl.weights(t, N, k, seed=2100 + 10 * t + h)
-            x = wl.activations(8, k, seed=2200 + 10 * t + h)
+            W = wl.weights(t, N, k, seed=2100 + 1000 * t + _pieces(t, h))
+            x = wl.activations(8, k, seed=2200 + 1000 * t + _pieces(t, h))
             y, a = oracle.matvec(t, W, x, N, k, 8)
             out[t, h] = dict(W=W, x=x, Wd=to_dev(W.ravel()), xd=to_dev(x.ravel()), y=y[0], a=a[0], k=k)
     return out
 
 
-@pytest.mark.parametrize("h", HALVES, ids=["1.5steps", "3.5steps"])
+@pytest.mark.parametrize("h", PIECES, ids=[str(p) for p in PIECES])
 @pytest.mark.parametrize("t", TYPES, ids=IDS)
 def test_half_step_rows_tolerance_and_row_exactness(t, h, data):
     d = data[t, h]
@@ -90,7 +98,7 @@ def _packings(t, kc_max):
 @pytest.mark.parametrize("m", [1, 3, 8])
 @pytest.mark.parametrize("t", TYPES, ids=IDS)
 def test_half_step_packing_is_inert(t, m, data):
-    for h in HALVES:
+    for h in PIECES:
         d = data[t, h]
         k = d["k"]
         sd = qfr.row_exact_schedule(t, N, k, m)
@@ -102,7 +110,7 @@ def test_half_step_packing_is_inert(t, m, data):
 
 @pytest.mark.parametrize("t", TYPES, ids=IDS)
 def test_half_step_pinned_split_within_tolerance(t, data):
-    d = data[t, 7]
+    d = data[t, 224]
     k, m = d["k"], 4
     sd = qfr.row_exact_schedule(t, N, k, m)
     for K in (2,):
@@ -113,7 +121,7 @@ def test_half_step_pinned_split_within_tolerance(t, data):
 
 @pytest.mark.parametrize("t", [wl.Q6_K, wl.Q8_0, wl.F16], ids=["Q6_K", "Q8_0", "F16"])
 def test_half_step_batched_and_gathered_equal_per_entry(t):
-    n, k, m, batch = 521, _k(t, 7), 5, 3
+    n, k, m, batch = 521, _k(t, 224), 5, 3
     assert qfr.row_exact_schedule(t, n, k, m, batch).k_split == 1
     W = wl.weights(t, n * batch, k, seed=2300 + t)
     s = Strides(k + 8, 5 * (k + 8), n + 3, 5 * (n + 3))
@@ -143,7 +151,7 @@ def test_half_step_batched_and_gathered_equal_per_entry(t):
 
 @pytest.mark.parametrize("t", [wl.Q6_K, wl.Q8_0, wl.BF16], ids=["Q6_K", "Q8_0", "BF16"])
 def test_half_step_fused_norm_one_kernel_equals_two_launches(t):
-    n, k = 600, _k(t, 7)
+    n, k = 600, _k(t, 224)
     W = wl.weights(t, n, k, seed=2500 + t)
     x = wl.activations(8, k, seed=2510 + t)
     r = wl.activations(8, k, seed=2520 + t)
