@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--split-sweep", default="",
                     help="write the skinny-output comparison (default schedule, its reduction split, against "
                          "the best single-wave-row packing) to this JSON file")
+    ap.add_argument("--lane-sweep", default="",
+                    help="write the lane-map comparison (default schedule, its lanes per row, against the best "
+                         "packing on the other lane map) for the half-step workloads to this JSON file")
     ap.add_argument("--profile-only", action="store_true",
                     help="launch the timed steps eagerly and exit (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -193,6 +196,10 @@ def main():
     if args.split_sweep:
         names = [v for v in args.sweep_workloads.split(",") if v] or None
         split_sweep(args.split_sweep, names)
+        return
+    if args.lane_sweep:
+        names = [v for v in args.sweep_workloads.split(",") if v] or None
+        lane_sweep(args.lane_sweep, names)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the mat-vec shards by weight rows with no "
@@ -804,6 +811,102 @@ def split_sweep(path, names=None):
                    "best_derived_split_us": round(med[best[d.k_split]], 3),
                    "unsplit_over_default": round(med[best[1]] / med[None], 4),
                    "candidates_timed": len(timed)}
+            res.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+        del Wd
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
+def lane_sweep(path, names=None):
+    """Rows whose last 64-lane wave step is at most half full: for every m of
+    each workload, the default schedule (lanes per row derived from the
+    weight type, k and the split) against pinned packings on the other lane
+    map (64 lanes per row where the default takes 32, 32 where it keeps 64;
+    the bits then differ, within the tolerance) and on the derived one: rows
+    per wave 1 / 2 / 4, 4 / 8 waves per workgroup, half, once and twice the
+    default's workgroups per batch entry or one row group per wave, the
+    default's LDS pass.  Each
+    timed as the mean of back-to-back launches on cold weights; then the
+    default and the best of each map again, in five interleaved rounds,
+    median per schedule."""
+    import ctypes
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import quantized_few_row_amd as qfr
+    import workloads as wl
+    names = names or list(wl.LANE_MAP)
+    lib = qfr.load_library()
+    stream = torch.cuda.Stream()
+    hs = stream.cuda_stream
+    res = []
+    for name in names:
+        w = wl.get(name)
+        t, n, k, batch = w.wtype, w.n, w.k, w.batch
+        xrs, xbs, yrs, ybs = w.strides(8)
+        st = qfr.Strides(xrs, xbs, yrs, ybs)
+        W = w.make_weights()
+        copies = max(2, int(np.ceil((1 << 30) / w.stored_weight_bytes)))
+        Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
+        wp = [Wd[c].data_ptr() for c in range(copies)]
+        xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        for m in sorted(set(w.ms) | {1, 2, 4, 8}):
+            _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, st)
+            y = torch.zeros(yb // 4, dtype=torch.float32, device="cuda")
+            d = qfr.row_exact_schedule(t, n, k, m, batch)
+            other = 32 if d.lanes_per_row == 64 else 64
+            cands = {}
+            wgs_set = sorted({max(1, d.workgroups_per_batch // 2), d.workgroups_per_batch,
+                              2 * d.workgroups_per_batch, 1 << 30})
+            for L in (d.lanes_per_row, other):
+                for nr in (1, 2, 4):
+                    for wv in (4, 8):
+                        for wgs in wgs_set:
+                            cands[(L, nr, wv, wgs)] = qfr.Schedule(d.k_split, nr, wv, wgs, d.k_chunk, L)
+
+            def run(s, i):
+                if s is None:
+                    return lib.row_exact_mv(t, wp[i % copies], xd.data_ptr(), y.data_ptr(), n, k, m, batch,
+                                            ctypes.byref(st), hs)
+                return lib.row_exact_mv_scheduled(t, wp[i % copies], xd.data_ptr(), y.data_ptr(), n, k, m, batch,
+                                                  ctypes.byref(st), ctypes.byref(s), hs)
+
+            def mean_us(s, reps=100):
+                with torch.cuda.stream(stream):
+                    for i in range(3):
+                        run(s, i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda._sleep(int(2e6))
+                    e0.record(stream)
+                    for i in range(reps):
+                        run(s, i)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / reps
+
+            timed = {}
+            for key, s in cands.items():
+                with torch.cuda.stream(stream):
+                    rc = run(s, 0)
+                torch.cuda.synchronize()
+                if rc:  # over the device's limits (refused before launch)
+                    continue
+                timed[key] = mean_us(s)
+            best = {L: min((key for key in timed if key[0] == L), key=timed.get) for L in {key[0] for key in timed}}
+            rounds = {None: [], **{b: [] for b in best.values()}}
+            for _ in range(5):
+                for key in rounds:
+                    rounds[key].append(mean_us(cands[key] if key else None))
+            med = {key: statistics.median(v) for key, v in rounds.items()}
+            bo, bd = best[other], best[d.lanes_per_row]
+            rec = {"workload": name, "m": m, "default": d.asdict(), "default_us": round(med[None], 3),
+                   "best_other_lanes": cands[bo].asdict(), "best_other_lanes_us": round(med[bo], 3),
+                   "best_derived_lanes": cands[bd].asdict(), "best_derived_lanes_us": round(med[bd], 3),
+                   "other_over_default": round(med[bo] / med[None], 4), "candidates_timed": len(timed)}
             res.append(rec)
             print(json.dumps(rec), file=sys.stderr, flush=True)
         del Wd

@@ -91,13 +91,13 @@ typedef struct {
 
 /* Launch schedule (RowExactMatvecSchedule, re-planned for CDNA4 wave64).
  *  k_split              : numerics.  Waves whose partial sums form one output:
- *                         1, 2, 4 or 8.  With 1 the 64 lanes of one wave
- *                         split the row and a fixed permlane/DPP tree adds
- *                         them; with K > 1 wave s of K takes the row's wave
- *                         steps s, s + K, s + 2K, ..., each wave's lanes are
- *                         added by the same tree, and the K wave sums by the
- *                         pairwise tree ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))
- *                         cut to K terms.  row_exact_schedule() derives it
+ *                         1, 2, 4 or 8.  With 1 the lanes_per_row lanes of
+ *                         one wave split the row and a fixed permlane/DPP
+ *                         tree adds them; with K > 1 (64 lanes per row) wave
+ *                         s of K takes the row's wave steps s, s + K, s + 2K,
+ *                         ..., each wave's lanes are added by the same tree,
+ *                         and the K wave sums by the pairwise tree
+ *                         ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) cut to K terms.  row_exact_schedule() derives it
  *                         from (weight type, k, n): the largest power of two
  *                         <= min(1024 / n, 8, whole 64-piece wave steps of
  *                         a row); 1 for rows of at most 32 pieces or fewer
@@ -120,6 +120,18 @@ typedef struct {
  *                         BF16, 256 for F32, 2048 for Q8_0 / Q5_0, 4096 for
  *                         Q4_K / Q6_K); with k_split > 1 a pass of fewer than
  *                         k_split wave steps leaves some waves idle.
+ *  lanes_per_row        : numerics.  Lanes of a wave that split one row
+ *                         (piece p of the row goes to lane p mod L; a wave
+ *                         covers 64 / L rows side by side): 16, 32 or 64, or
+ *                         0 for the value derived from (weight type, k,
+ *                         k_split).  row_exact_schedule() gives the derived
+ *                         value: 16 / 32 for rows of at most 16 / 32 pieces;
+ *                         32 for rows of Q8_0, Q4_K, Q6_K and Q5_0 of 64 s + r
+ *                         pieces, 0 < r <= 32, with k_split 1 and under 2^29
+ *                         bytes (their last 64-lane step would be at most
+ *                         half full); 64 otherwise.  A pinned value gives
+ *                         that lane map's sums; below 64 it needs k_split 1
+ *                         and (64 / L) * rows_per_wave * row bytes < 2^32.
  * Packing fields never change the bits of y. */
 typedef struct {
     uint32_t k_split;
@@ -127,6 +139,7 @@ typedef struct {
     uint32_t waves_per_workgroup;
     uint32_t workgroups_per_batch;
     uint32_t k_chunk;
+    uint32_t lanes_per_row;
 } row_exact_schedule_t;
 
 /* Error codes. */
@@ -161,10 +174,12 @@ int row_exact_mv(row_exact_weight_t wt, const void *W, const float *x, float *y,
 
 /* As row_exact_mv with an explicit schedule
  * (dispatch_row_exact_matvec_scheduled).  Outputs are bitwise identical to
- * row_exact_mv's for every valid schedule with the derived k_split: packing
- * is inert; another k_split gives that split's sums.  Extra error:
+ * row_exact_mv's for every valid schedule with the derived k_split and
+ * lanes_per_row: packing is inert; another k_split or lane count gives that
+ * reduction's sums.  Extra error:
  * ROW_EXACT_ESCHEDULE (a field out of range, k_split not dividing the waves
- * or above the row's wave steps, k_chunk not a wave-step multiple, LDS need
+ * or above the row's wave steps, k_chunk not a wave-step multiple,
+ * lanes_per_row below 64 with k_split > 1 or rows too long for it, LDS need
  * above the device limit). */
 int row_exact_mv_scheduled(row_exact_weight_t wt, const void *W, const float *x, float *y, uint32_t n,
                            uint32_t k, uint32_t m, uint32_t batch, const row_exact_strides_t *strides,
@@ -310,11 +325,12 @@ int row_exact_mv_add_rmsnorm_noalloc(row_exact_weight_t wt, const void *W, const
                                      hipStream_t stream);
 
 /* Default schedule for a shape (RowExactMatvecSchedule::for_device).  k_split
- * depends on (wt, k, n) only; the packing fields may depend on every argument
- * and on the current device.  Unlike the page's query (weight, rows, k), this
+ * depends on (wt, k, n) only, lanes_per_row on (wt, k, k_split); the packing
+ * fields may depend on every argument and on the current device.  Unlike the page's query (weight, rows, k), this
  * one takes m: the packing is chosen per m because the m-row kernel's
  * register and LDS needs decide how many rows a wave and how many workgroups
- * a CU can hold.  m never reaches k_split, so outputs stay row-exact.
+ * a CU can hold.  m never reaches k_split or lanes_per_row, so outputs stay
+ * row-exact.
  * Writes *out; errors: EARG, EHIP. */
 int row_exact_schedule(row_exact_weight_t wt, uint32_t n, uint32_t k, uint32_t m, uint32_t batch,
                        row_exact_schedule_t *out);

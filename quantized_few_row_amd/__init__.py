@@ -61,7 +61,7 @@ class Schedule(ctypes.Structure):
     """``row_exact_schedule_t``."""
     _fields_ = [("k_split", ctypes.c_uint32), ("rows_per_wave", ctypes.c_uint32),
                 ("waves_per_workgroup", ctypes.c_uint32), ("workgroups_per_batch", ctypes.c_uint32),
-                ("k_chunk", ctypes.c_uint32)]
+                ("k_chunk", ctypes.c_uint32), ("lanes_per_row", ctypes.c_uint32)]
 
     def asdict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -407,6 +407,7 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     if (rc) return rc;
     const uint64_t rows = (uint64_t)n * batch;
     s.k_split = derived_k_split(t, k, n);
+    s.lanes_per_row = 1u << lane_map_log2(t, k, s.k_split);
     const uint32_t step = wave_step_values(t);
     if (s.k_split > 1) {
         // Skinny outputs, K waves per row group: max(4, K) waves per
@@ -547,6 +548,16 @@ int check_schedule_fields(int t, uint32_t k, const row_exact_schedule_t &s) {
                     K, pieces_of(t, k) / 64, type_name(t), k);
     if (!(s.rows_per_wave == 1 || s.rows_per_wave == 2 || s.rows_per_wave == 4))
         return fail(ROW_EXACT_ESCHEDULE, "schedule rows_per_wave (%u) must be 1, 2 or 4", s.rows_per_wave);
+    const uint32_t L = s.lanes_per_row;
+    if (!(L == 0 || L == 16 || L == 32 || L == 64))
+        return fail(ROW_EXACT_ESCHEDULE, "schedule lanes_per_row (%u) must be 0 (derived), 16, 32 or 64", L);
+    if (L && L < 64 && K > 1)
+        return fail(ROW_EXACT_ESCHEDULE, "schedule lanes_per_row (%u): a k_split (%u) needs 64 lanes per row", L, K);
+    if (L && L < 64 && (uint64_t)(64 / L) * s.rows_per_wave * row_bytes_of(t, k) >= (1ull << 32))
+        return fail(ROW_EXACT_ESCHEDULE,
+                    "schedule lanes_per_row (%u) with rows_per_wave (%u): %s rows of k = %u are too long for the "
+                    "32-bit row offsets of a wave's row slots",
+                    L, s.rows_per_wave, type_name(t), k);
     if (s.waves_per_workgroup < 1 || s.waves_per_workgroup > 8)
         return fail(ROW_EXACT_ESCHEDULE, "schedule waves_per_workgroup (%u) must be 1 to 8", s.waves_per_workgroup);
     if (s.waves_per_workgroup % K)
@@ -671,7 +682,8 @@ int plan_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t
     a.xrs = s.x_row_stride;
     a.yrs = s.y_row_stride;
     a.pieces = pieces_of(t, k);
-    a.lpr_log2 = lane_map_log2(t, k, sch.k_split);
+    a.lpr_log2 = sch.lanes_per_row == 16 ? 4u : sch.lanes_per_row == 32 ? 5u : sch.lanes_per_row == 64 ? 6u
+                                                                       : lane_map_log2(t, k, sch.k_split);
     const uint32_t nr = sch.rows_per_wave;
     const uint32_t rg = nr << (6 - a.lpr_log2);  // rows per group: NR rows in each of the wave's slots
     a.groups_per_batch = (n + rg - 1) / rg;

@@ -206,6 +206,10 @@ def test_output_must_not_overlap_inputs():
     (Schedule(1, 1, 9, 1, 1 << 30), "waves_per_workgroup"),
     (Schedule(1, 1, 8, 0, 1 << 30), "workgroups_per_batch"),
     (Schedule(1, 1, 8, 4, 1000), "k_chunk"),
+    (Schedule(1, 1, 8, 4, 1 << 30, 8), "lanes_per_row (8) must be 0 (derived), 16, 32 or 64"),
+    (Schedule(1, 1, 8, 4, 1 << 30, 48), "lanes_per_row (48) must be"),
+    (Schedule(1, 1, 8, 4, 1 << 30, 128), "lanes_per_row (128) must be"),
+    (Schedule(2, 1, 8, 4, 1 << 30, 32), "lanes_per_row (32): a k_split (2) needs 64 lanes per row"),
 ])
 def test_invalid_schedule(sched, text):
     rc, msg = _mv(k=4096, schedule=sched)
@@ -216,6 +220,18 @@ def test_k_split_needs_rows_of_64_lanes():
     # F16 rows of k = 256 are 32 pieces (32 lanes per row): never split
     rc, msg = _mv(wt=Weight.F16, k=256, schedule=Schedule(2, 1, 8, 1, 1 << 30))
     assert rc == -6 and "k_split (2): F16 rows of k = 256 (at most 32 pieces) are not split" in msg, msg
+
+
+def test_lanes_per_row_limited_by_row_offsets():
+    # a lane addresses the rows of its wave's slots by 32-bit offsets: (64 /
+    # lanes) * rows_per_wave * row bytes must stay below 2^32.  Q8_0 rows of
+    # k = 2^28 are 285,212,672 bytes: 16 lanes x 4 rows (16 row offsets) pass
+    # 2^32 bytes and are refused; 64 lanes are always fine.
+    big = 1 << 28
+    rc, msg = _mv(n=8, k=big, m=1, schedule=Schedule(1, 4, 8, 1, 2048, 16))
+    assert rc == -6 and "too long for the 32-bit row offsets" in msg, msg
+    rc, msg = _mv(n=8, k=big, m=1, schedule=Schedule(1, 4, 8, 1, 2048, 64))
+    assert "lanes_per_row" not in msg, msg
 
 
 def test_null_schedule():

@@ -168,3 +168,31 @@ def test_half_step_fused_norm_one_kernel_equals_two_launches(t):
         assert np.array_equal(bits(h), href[:m * k].view(np.int32)), f"m={m}: h"
         check_tolerance(y1.cpu().numpy().reshape(1, m, n), yref[:, :m], a[:, :m], f"m={m}")
         assert np.array_equal(bits(y1), bits(y2)), f"m={m}: one kernel and two launches differ"
+
+
+@pytest.mark.parametrize("h", (96, 224))
+@pytest.mark.parametrize("t", TYPES, ids=IDS)
+def test_pinned_lanes_per_row(t, h, data):
+    """Each lane map pinned (16, 32, 64 lanes per row, unsplit): within the
+    tolerance at m = 1 and 8, every row of m = 8 bitwise equal to its m = 1
+    result under the same map, two packings at m = 3 bitwise equal; the
+    derived value pinned gives the default call's bits."""
+    d = data[t, h]
+    k = d["k"]
+    derived = qfr.row_exact_schedule(t, N, k, 1).lanes_per_row
+    one = lambda L: Schedule(1, 1, 8, 1000, 1 << 30, L)       # noqa: E731
+    passes = lambda nr, wv, kc, L: Schedule(1, nr, wv, 1000, kc, L)  # noqa: E731
+    for L in (16, 32, 64):
+        ones = [bits(run_mv(t, d["Wd"], d["xd"][j * k:], N, k, 1, schedule=one(L))) for j in range(8)]
+        check_tolerance(np.stack([o.view(np.float32) for o in ones]), d["y"], d["a"], f"L={L} m=1")
+        y8 = run_mv(t, d["Wd"], d["xd"], N, k, 8, schedule=passes(1, 8, STEP[t], L))
+        check_tolerance(y8.cpu().numpy().reshape(8, N), d["y"], d["a"], f"L={L} m=8")
+        yb = bits(y8).reshape(8, N)
+        for j in range(8):
+            assert np.array_equal(yb[j], ones[j]), f"L={L}: m=8 row {j} differs from its m=1 result"
+        a = bits(run_mv(t, d["Wd"], d["xd"], N, k, 3, schedule=passes(1, 8, STEP[t], L)))
+        b = bits(run_mv(t, d["Wd"], d["xd"], N, k, 3, schedule=passes(2, 4, 2 * STEP[t], L)))
+        assert np.array_equal(a, b), f"L={L}: packing changed the bits"
+        if L == derived:
+            assert np.array_equal(ones[0], bits(run_mv(t, d["Wd"], d["xd"], N, k, 1))), \
+                f"L={L} pinned differs from the default call"

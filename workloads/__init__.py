@@ -250,8 +250,21 @@ SKINNY_WORKLOADS: List[Workload] = [
     Workload("q6_k_32x14336", Q6_K, 32, 14336, 1, (1, 4, 8), 17),
 ]
 WORKLOADS += SKINNY_WORKLOADS
+# Rows whose last 64-lane wave step is at most half full (64 s + r pieces,
+# 0 < r <= 32): the block types take 32 lanes per row there, the dense ones
+# keep 64 (bench.py --lane-sweep times both maps).
+LANE_MAP_WORKLOADS: List[Workload] = [
+    Workload("q8_0_4096x3072", Q8_0, 4096, 3072, 1, (1, 2, 4, 8), 18),
+    Workload("q8_0_4096x11008", Q8_0, 4096, 11008, 1, (1, 2, 4, 8), 19),
+    Workload("q4_k_4096x4352", Q4_K, 4096, 4352, 1, (1, 2, 4, 8), 20),
+    Workload("q6_k_4096x6144", Q6_K, 4096, 6144, 1, (1, 2, 4, 8), 21),
+    Workload("q5_0_16x1024x11008_grouped", Q5_0, 1024, 11008, 16, (1, 2, 4, 8), 22, grouped=True),
+    Workload("f16_4096x1792", F16, 4096, 1792, 1, (1, 2, 4, 8), 23),
+]
+WORKLOADS += LANE_MAP_WORKLOADS
 HELD_OUT = ("q4_k_1024x2816", "q8_0_2816x2112")
 SKINNY = tuple(w.name for w in SKINNY_WORKLOADS)
+LANE_MAP = ("q6_k_4096x14336",) + tuple(w.name for w in LANE_MAP_WORKLOADS)
 BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
 
 
