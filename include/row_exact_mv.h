@@ -16,10 +16,10 @@
  *
  * Row exactness: output row j is bitwise identical whether it is computed with
  * m = 1 or as one row of any m <= 8, and identical across repeated calls.  The
- * only thing that changes the bits of an output is the reduction split
- * (row_exact_schedule_t.k_split), which the library derives from the weight
- * type, k and the rows n of one batch entry (never from m or the batch);
- * every other schedule field only packs work.
+ * only things that change the bits of an output are the reduction split and
+ * the lanes per row (row_exact_schedule_t.k_split, .lanes_per_row), which the
+ * library derives from the weight type, k and the rows n of one batch entry
+ * (never from m or the batch); every other schedule field only packs work.
  *
  * Conventions for every entry point:
  *  - Pointers W, x, y, out are device pointers (HBM).  The caller owns them;
