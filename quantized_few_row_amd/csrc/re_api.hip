@@ -122,9 +122,10 @@ int device_info(DevInfo &out) {
     return 0;
 }
 
-// Floats per staged x row for kc values (4 pad floats per pad period).
-uint32_t xs_stride(int t, uint32_t kc) {
-    const uint32_t padp = pad_period(t);
+// Floats per staged x row for kc values of an m-row product (4 pad floats
+// per pad period).
+uint32_t xs_stride(int t, uint32_t kc, uint32_t m) {
+    const uint32_t padp = pad_period(t, m);
     return kc + 4 * ((kc + padp - 1) / padp);
 }
 
@@ -132,7 +133,7 @@ uint32_t xs_stride(int t, uint32_t kc) {
 // the fused normalisation's per-row partial sums.
 size_t lds_x_bytes(int t, uint32_t m, uint32_t k, uint32_t k_chunk) {
     const uint32_t kc = k_chunk < k ? k_chunk : k;
-    return (size_t)m * xs_stride(t, kc) * sizeof(float);
+    return (size_t)m * xs_stride(t, kc, m) * sizeof(float);
 }
 // Floats per input row of the segment sums (Q4_K: one per 32 staged values).
 uint32_t sx_stride(int t, uint32_t k, uint32_t k_chunk) {
@@ -701,7 +702,7 @@ int plan_mv(int t, const void *W, const float *x, float *y, uint32_t n, uint32_t
         a.pieces_per_chunk = sch.k_chunk / step * 64;
         a.nchunks = (a.pieces + a.pieces_per_chunk - 1) / a.pieces_per_chunk;
     }
-    a.xs_stride = xs_stride(t, a.kchunk);
+    a.xs_stride = xs_stride(t, a.kchunk, m);
     a.ids = ids;
     a.num_experts = num_experts;
     a.r = norm ? norm->r : nullptr;

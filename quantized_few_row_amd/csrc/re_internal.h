@@ -157,6 +157,17 @@ inline uint32_t lanes_per_row_log2(int t, uint32_t k) {
     const uint32_t p = pieces_of(t, k);
     return p <= 16 ? 4u : p <= 32 ? 5u : 6u;
 }
+// 1: from m = 2 on, Q6_K's staged x is piece-major (each piece's 64 values
+// contiguous in the piece's value order, 4 pad floats after each piece: 68
+// floats per piece, the density of a 64-value pad period), so that the
+// lanes' reads of one group of sixteen consecutive pieces hit distinct LDS
+// banks; at m = 1 it keeps the value order, whose LDS-DMA staging reads x
+// contiguously.  A staging layout only: the bits do not depend on it.
+#ifndef REX_Q6K_PIECE_MAJOR
+#define REX_Q6K_PIECE_MAJOR 1
+#endif
+__host__ __device__ constexpr bool piece_major(int t, uint32_t m) { return REX_Q6K_PIECE_MAJOR && t == kQ6K && m >= 2; }
+
 inline uint32_t pad_period(int t) {
     switch (t) {
     case kF16: return Geo<kF16>::PADP;
@@ -167,6 +178,11 @@ inline uint32_t pad_period(int t) {
     case kBF16: return Geo<kBF16>::PADP;
     default: return Geo<kQ5_0>::PADP;
     }
+}
+// Values per pad period of a staged x row (piece-major rows: one piece).
+inline uint32_t pad_period(int t, uint32_t m) {
+    if (piece_major(t, m)) return 64;
+    return pad_period(t);
 }
 
 // Launchers, one translation unit per weight type.

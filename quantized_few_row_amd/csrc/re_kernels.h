@@ -677,6 +677,50 @@ __device__ __forceinline__ void reduce_store_split(const float (&acc)[NR][M], fl
 
 // ---------------------------------------------------------------- x staging
 
+// Float offset, in a staged input row of an M-row product, of value lv (a
+// multiple of 4, counted from the pass' first value): value order with 4 pad
+// floats after every Geo<T>::PADP values, or, piece-major (piece_major:
+// Q6_K from M = 2), piece q's 64 values (its four 16-value runs, in order)
+// at 68 q, followed by 4 pad floats.
+template <int T, int M> __device__ __forceinline__ uint32_t lpos(uint32_t lv) {
+    if constexpr (piece_major(T, M)) {
+        const uint32_t r = lv & 255u;  // value in its super-block
+        const uint32_t piece = 4 * (lv >> 8) + 2 * (r >> 7) + ((r >> 4) & 1u);
+        return 68 * piece + 16 * ((r >> 5) & 3u) + (r & 15u);
+    } else {
+        return lv + 4 * (lv / Geo<T>::PADP);
+    }
+}
+
+// Data slots (16 bytes) per pad period of a staged row.
+template <int T, int M> constexpr uint32_t slots_per_period() { return piece_major(T, M) ? 16u : Geo<T>::PADP / 4; }
+
+// The 4-value chunk of the input row (its first value / 4, from the pass'
+// first value) held by data slot r of pad period per of a staged row: the
+// inverse of lpos on 16-byte slots.
+template <int T, int M> __device__ __forceinline__ uint32_t slot_chunk(uint32_t per, uint32_t r) {
+    if constexpr (piece_major(T, M)) {
+        // per = piece (super-block per / 4, quarter per % 4), r = 4 t + w4
+        return 64 * (per >> 2) + 32 * ((per >> 1) & 1u) + 8 * (r >> 2) + 4 * (per & 1u) + (r & 3u);
+    } else {
+        return per * slots_per_period<T, M>() + r;
+    }
+}
+
+// LDS offset of piece p's staged values (pass' first value vb) and of its
+// group g: the type's value-order offsets, or, piece-major, 68 (p - vb / 64)
+// and 4 g (sixteen consecutive pieces then start on sixteen distinct 4-bank
+// groups of the 64 LDS banks, so a wave's reads of one group do not
+// conflict).
+template <int T, int M> __device__ __forceinline__ uint32_t xoff_of(uint32_t p, uint32_t vb) {
+    if constexpr (piece_major(T, M)) return 68 * (p - vb / 64);
+    else return Tr<T>::xoff(p, vb);
+}
+template <int T, int M> __device__ __forceinline__ constexpr uint32_t goff_of(int g) {
+    if constexpr (piece_major(T, M)) return 4 * g;
+    else return Tr<T>::goff(g);
+}
+
 // Stage values [v0, v1) of the m input rows into LDS.
 template <int T, int M>
 __device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
@@ -700,7 +744,7 @@ __device__ __forceinline__ void stage_x(float *__restrict__ xs, const float *__r
             const uint32_t q = q0 + u * nt;
             if (q < n4) {
                 const uint32_t lv = 4 * q;
-                const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+                const uint32_t d = lpos<T, M>(lv);
 #pragma unroll
                 for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = v[u][j];
             }
@@ -740,7 +784,7 @@ __device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const floa
         const uint32_t q = threadIdx.x + u * nt;
         if (q < n4) {
             const uint32_t lv = 4 * q;
-            const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+            const uint32_t d = lpos<T, M>(lv);
 #pragma unroll
             for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = v[u][j];
         }
@@ -748,7 +792,7 @@ __device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const floa
     // the rest (k > 4 U nt), behind the weights
     for (uint32_t q = threadIdx.x + U * nt; q < n4; q += nt) {
         const uint32_t lv = 4 * q;
-        const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+        const uint32_t d = lpos<T, M>(lv);
 #pragma unroll
         for (int j = 0; j < M; ++j) *(f32x4 *)(xs + j * XS + d) = *(const f32x4 *)(xb + (uint64_t)j * xrs + lv);
     }
@@ -761,9 +805,10 @@ __device__ __forceinline__ void stage_x_first(float *__restrict__ xs, const floa
 // (see the host's x_dma), for the types whose Tr<T>::LOADS gives the fixed
 // number of load instructions of a piece (Q6_K); the others keep the
 // register staging: the extra code path cost them 1-9% at m = 1 on MI355X.  Each wave
-// instruction fills 64 consecutive 16-byte slots of one staged row in the
-// padded layout (Geo<T>::PADP values, then one pad slot); a lane reads the
-// x chunk its slot holds, pad slots and slots past the row are masked off.
+// instruction fills 64 consecutive 16-byte slots of one staged row (pad
+// periods of Geo<T>::PADP / 4 data slots and one pad slot); a lane reads the
+// x chunk its slot holds (slot_chunk), pad slots and slots past the row are
+// masked off.
 // Completion is counted by vmcnt with the other loads, in issue order: the
 // caller waits with barrier_after_loads, never with __syncthreads.
 __device__ __forceinline__ void lds_dma16(const float *src, float *lds) {
@@ -773,7 +818,7 @@ __device__ __forceinline__ void lds_dma16(const float *src, float *lds) {
 template <int T, int M>
 __device__ __forceinline__ void stage_x_dma(float *__restrict__ xs, const float *__restrict__ xb, uint32_t xrs,
                                             uint32_t k, uint32_t XS, uint32_t wave, uint32_t nwaves, uint32_t lane) {
-    constexpr uint32_t P = Geo<T>::PADP / 4;  // data slots per pad period
+    constexpr uint32_t P = slots_per_period<T, M>();  // data slots per pad period
     const uint32_t S = XS / 4;                 // slots per staged row
     const uint32_t bpr = (S + 63) >> 6;        // 64-slot blocks per row
     const uint32_t n4 = k >> 2;
@@ -781,7 +826,7 @@ __device__ __forceinline__ void stage_x_dma(float *__restrict__ xs, const float 
         const uint32_t j = t / bpr, b = t - j * bpr;
         const uint32_t s = (b << 6) + lane;
         const uint32_t per = s / (P + 1), r = s - per * (P + 1);
-        const uint32_t d = per * P + r;
+        const uint32_t d = slot_chunk<T, M>(per, r);
         if (r < P && d < n4) lds_dma16(xb + (uint64_t)j * xrs + 4 * d, xs + j * XS + (b << 8));
     }
 }
@@ -820,7 +865,7 @@ __device__ __forceinline__ void stage_sx(const float *__restrict__ xs, uint32_t 
     for (uint32_t i = threadIdx.x; i < M * nseg; i += blockDim.x) {
         const uint32_t j = i / nseg, sg = i - j * nseg;
         const uint32_t lv = 32 * sg;
-        const float *__restrict__ src = xs + j * XS + lv + 4 * (lv / Geo<T>::PADP);
+        const float *__restrict__ src = xs + j * XS + lpos<T, M>(lv);
         f32x4 v[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] = *(const f32x4 *)(src + 4 * c);
@@ -944,7 +989,7 @@ __device__ __forceinline__ void norm_partials(double *part, float *__restrict__ 
 #pragma unroll
                                         for (int e = 0; e < 4; ++e) u[e] = h[e] * gv[c][e];
                                     }
-                                    *(f32x4 *)(xs + j * XS + lv + 4 * (lv / Geo<T>::PADP)) = u;
+                                    *(f32x4 *)(xs + j * XS + lpos<T, M>(lv)) = u;
                                 }
                                 ss[i] = fold4(ss[i], h);
                             }
@@ -977,7 +1022,7 @@ __device__ __forceinline__ void stage_u(float *__restrict__ xs, const float *__r
     for (uint32_t q = threadIdx.x; q < n4; q += blockDim.x) {
         const uint32_t v = v0 + 4 * q;
         const uint32_t lv = 4 * q;
-        const uint32_t d = lv + 4 * (lv / Geo<T>::PADP);
+        const uint32_t d = lpos<T, M>(lv);
 #pragma unroll
         for (int j = 0; j < M; ++j) {
             const f32x4 xv = *(const f32x4 *)(xb + (uint64_t)j * xrs + v);
@@ -1005,7 +1050,7 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
     typename TR::Pre pre[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) pre[r] = TR::prep(raw[r], p);
-    const float *__restrict__ xp = xs + TR::xoff(p, vb);
+    const float *__restrict__ xp = xs + xoff_of<T, M>(p, vb);
     if constexpr (TR::SEG == 0) {
         // unscaled: acc = fma(w, x, acc) value by value
 #pragma unroll
@@ -1013,7 +1058,7 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
             if (!TR::group_valid(p, g, k)) continue;
             f32x4 xv[M];
 #pragma unroll
-            for (int j = 0; j < M; ++j) xv[j] = *(const f32x4 *)(xp + j * XS + TR::goff(g));
+            for (int j = 0; j < M; ++j) xv[j] = *(const f32x4 *)(xp + j * XS + goff_of<T, M>(g));
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 float w[4];
@@ -1033,7 +1078,7 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
         // scheduler is kept from hoisting further reads (register pressure).
         f32x4 xv[2][M];
 #pragma unroll
-        for (int j = 0; j < M; ++j) xv[0][j] = *(const f32x4 *)(xp + j * XS + TR::goff(0));
+        for (int j = 0; j < M; ++j) xv[0][j] = *(const f32x4 *)(xp + j * XS + goff_of<T, M>(0));
         float part[NR][M];
         // the sums of x over the piece's two segments (offset types)
         f32x2 sv[M];
@@ -1046,7 +1091,7 @@ __device__ __forceinline__ void compute_piece(float (&acc)[NR][M], const typenam
             const int gg = g % TR::SEG, cb = g & 1;
             if (g + 1 < TR::NG) {
 #pragma unroll
-                for (int j = 0; j < M; ++j) xv[cb ^ 1][j] = *(const f32x4 *)(xp + j * XS + TR::goff(g + 1));
+                for (int j = 0; j < M; ++j) xv[cb ^ 1][j] = *(const f32x4 *)(xp + j * XS + goff_of<T, M>(g + 1));
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {

@@ -196,3 +196,40 @@ def test_pinned_lanes_per_row(t, h, data):
         if L == derived:
             assert np.array_equal(ones[0], bits(run_mv(t, d["Wd"], d["xd"], N, k, 1))), \
                 f"L={L} pinned differs from the default call"
+
+
+def _rule_lanes(t, k, K):
+    """The documented lane map: 16 / 32 for rows of at most 16 / 32 pieces;
+    32 for unsplit block-type rows of 64 s + r pieces, 0 < r <= 32, under
+    2^29 bytes; 64 otherwise."""
+    p = k // (STEP[t] // 64)
+    if p <= 16:
+        return 16
+    if p <= 32:
+        return 32
+    blocks = t in (wl.Q8_0, wl.Q4_K, wl.Q6_K, wl.Q5_0)
+    if blocks and K == 1 and 0 < p % 64 <= 32 and qfr.row_exact_row_bytes(t, k) < (1 << 29):
+        return 32
+    return 64
+
+
+@pytest.mark.parametrize("t", TYPES, ids=IDS)
+def test_derived_lanes_follow_the_rule(t):
+    """row_exact_schedule's lanes_per_row against the documented rule over
+    row lengths of 1..9 wave steps with every tail class, several n (split
+    and unsplit) and every m (the lane map never depends on m)."""
+    vpp = STEP[t] // 64
+    quantum = 4 if t in (wl.Q4_K, wl.Q6_K) else 1  # pieces per 256-value super-block
+    checked = 0
+    for p in sorted({quantum * i for i in range(1, 160 // quantum)} | {64 * s + r for s in range(1, 9)
+                                                                        for r in (quantum, 16, 32, 36, 60)}):
+        if p % quantum:
+            continue
+        k = p * vpp
+        for n in (1, 40, 300, 1024, 5000):
+            lanes = {qfr.row_exact_schedule(t, n, k, m).lanes_per_row for m in (1, 3, 8)}
+            assert len(lanes) == 1, f"p={p} n={n}: lanes depend on m: {lanes}"
+            K = qfr.row_exact_schedule(t, n, k, 1).k_split
+            assert lanes == {_rule_lanes(t, k, K)}, f"p={p} k={k} n={n} K={K}: {lanes}"
+            checked += 1
+    assert checked > 100
