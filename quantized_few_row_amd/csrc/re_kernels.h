@@ -175,9 +175,10 @@ template <> struct Tr<kF16> : Geo<kF16> {
         w[3] = h2f(r.w[2 * g + 1] >> 16);
     }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 8 * p + 4 * g; }
+    // 4 pad floats after every Geo PADP values (PADP / 8 pieces)
     static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
         const uint32_t q = p - vb / 8;
-        return 8 * q + 4 * (q / 4);
+        return 8 * q + 4 * (q / (Geo<kF16>::PADP / 8));
     }
     static constexpr uint32_t goff(int g) { return 4 * g; }
     static __device__ __forceinline__ bool group_valid(uint32_t p, int g, uint32_t k) {
@@ -236,10 +237,10 @@ template <> struct Tr<kF32> : Geo<kF32> {
         for (int i = 0; i < 4; ++i) w[i] = __uint_as_float(r.w[i]);
     }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int) { return 4 * p; }
-    // PADP 32: 4 pad floats after every 8 pieces
+    // 4 pad floats after every Geo PADP values (PADP / 4 pieces)
     static __device__ __forceinline__ uint32_t xoff(uint32_t p, uint32_t vb) {
         const uint32_t q = p - vb / 4;
-        return 4 * q + 4 * (q / 8);
+        return 4 * q + 4 * (q / (Geo<kF32>::PADP / 4));
     }
     static constexpr uint32_t goff(int) { return 0; }
     static __device__ __forceinline__ bool group_valid(uint32_t, int, uint32_t) { return true; }
