@@ -480,18 +480,15 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         s.workgroups_per_batch = (uint32_t)(w < max_wgs ? w : max_wgs);
         return 0;
     }
-    // rows per wave: the most that still leaves 8 waves per CU.  Q6_K rows
-    // on 32 lanes (two row slots per wave) in several LDS passes count as on
-    // 64 from m = 7, so each x value read from LDS feeds two rows per slot
-    // (4096 x 14336 at m = 8: -5%; at m = 5, 6 and for Q4_K and Q8_0 rows of
-    // 3.5 steps at m = 5 and 8, one row per slot is 4-16% faster)
+    // rows per wave: the most that still leaves 8 waves per CU (counted in
+    // row slots: 32-lane rows of several steps take one row per slot, which
+    // measured 4-16% faster than two for Q4_K, Q6_K and Q8_0 rows of 224
+    // pieces at m = 5..8)
     const uint64_t target_waves = (uint64_t)di.cus * 8;
     const uint32_t lpr = lane_map_log2(t, k, 1);
     const uint64_t wave_rows = rows >> (6 - lpr);
-    const bool long_sub = lpr < 6 && pieces_of(t, k) > 32;
-    const uint64_t nr_rows = (long_sub && t == kQ6K && m >= 7 && kc < k) ? rows : wave_rows;
     uint32_t nr = max_rows_per_wave(t, m);
-    while (nr > 1 && nr_rows / nr < target_waves) nr >>= 1;
+    while (nr > 1 && wave_rows / nr < target_waves) nr >>= 1;
     // Up to 4 input rows and fewer than 16 rows per wave: single rows for
     // rows of several wave steps, so each wave walks more items with loads
     // in flight behind the multiply (3-10% faster than 2 or 4 rows per wave
