@@ -78,14 +78,40 @@ def parse():
     return ap.parse_args()
 
 
+def _code_tokens(text):
+    """C/C++ source without its comments, whitespace runs collapsed (string
+    and character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources; traffic counters are reported only for the build they were taken on."""
+    """Hash of the HIP sources' code (comments and whitespace left out);
+    traffic counters are reported only for the code they were taken on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_few_row_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

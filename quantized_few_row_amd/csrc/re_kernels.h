@@ -9,8 +9,8 @@
 //     nibble bytes, two sub-blocks, of a super-block; Q6_K: a quarter
 //     super-block).  A row has 64 lanes of a wave, or 32 / 16 (two / four
 //     rows per wave) for rows of at most 32 / 16 pieces and, for the
-//     block-quantized types, rows whose pieces would leave the last 64-lane
-//     step half empty.  Lane L of the row's L_row lanes takes pieces L,
+//     block-quantized types, unsplit rows whose last 64-lane step would be
+//     at most half full.  Lane L of the row's L_row lanes takes pieces L,
 //     L + L_row, L + 2 L_row, ... in that order, so each load instruction of
 //     a wave covers adjacent bytes of each of its rows.
 //   - A wave streams rows_per_wave (NR) rows at once: every input value read

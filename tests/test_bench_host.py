@@ -89,3 +89,20 @@ def test_host_threads_stay_within_one_gpu_share():
 def test_copy_calibration_size_is_whole_vectors():
     assert bench.copy_calibration_bytes(256) == 256 << 20
     assert bench.copy_calibration_bytes(0.001) % 16 == 0
+
+
+def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    """Counters stay attached to the kernel code: comment and whitespace
+    edits keep the hash, a code edit (even inside a string) changes it."""
+    csrc = tmp_path / "quantized_few_row_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = 'int f(int a) { // one\n  return a + 1; /* two */ }\nconst char *s = "x // y";\n'
+    (csrc / "k.hip").write_text(src)
+    h0 = bench.kernel_source_hash()
+    (csrc / "k.hip").write_text(src.replace("// one", "// another comment").replace("  return", "\treturn"))
+    assert bench.kernel_source_hash() == h0
+    (csrc / "k.hip").write_text(src.replace("a + 1", "a + 2"))
+    assert bench.kernel_source_hash() != h0
+    (csrc / "k.hip").write_text(src.replace('"x // y"', '"x // z"'))
+    assert bench.kernel_source_hash() != h0
