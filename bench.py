@@ -66,6 +66,12 @@ def parse():
     ap.add_argument("--lane-sweep", default="",
                     help="write the lane-map comparison (default schedule, its lanes per row, against the best "
                          "packing on the other lane map) for the half-step workloads to this JSON file")
+    ap.add_argument("--ab", default="",
+                    help="another build of the library (python -m quantized_few_row_amd._build --out PATH -D ...): "
+                         "time the default calls of both builds, interleaved, for the workloads named with "
+                         "--sweep-workloads and write the results to --ab-out")
+    ap.add_argument("--ab-out", default="ab.json", help="JSON file for --ab")
+    ap.add_argument("--ab-ms", default="1,2,4,8", help="comma-separated input row counts for --ab")
     ap.add_argument("--profile-only", action="store_true",
                     help="launch the timed steps eagerly and exit (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
@@ -226,6 +232,10 @@ def main():
     if args.lane_sweep:
         names = [v for v in args.sweep_workloads.split(",") if v] or None
         lane_sweep(args.lane_sweep, names)
+        return
+    if args.ab:
+        names = [v for v in args.sweep_workloads.split(",") if v] or None
+        ab_compare(args.ab, args.ab_out, names, [int(v) for v in args.ab_ms.split(",") if v])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the mat-vec shards by weight rows with no "
@@ -939,6 +949,90 @@ def lane_sweep(path, names=None):
         torch.cuda.empty_cache()
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
+
+
+def ab_compare(other_path, path, names=None, ms=(1, 2, 4, 8)):
+    """The same default calls through this package's library (A) and another
+    build of it (B, e.g. one with a code-generation switch overridden): for
+    every workload and m, both outputs compared bit for bit, then five
+    interleaved rounds of back-to-back launches on cold weights per build,
+    median per build."""
+    import ctypes
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import quantized_few_row_amd as qfr
+    import workloads as wl
+    names = names or list(wl.LANE_MAP)
+    libs = {"a": qfr.load_library(), "b": qfr.load_variant(other_path)}
+    stream = torch.cuda.Stream()
+    hs = stream.cuda_stream
+    res = []
+    for name in names:
+        w = wl.get(name)
+        t, n, k, batch = w.wtype, w.n, w.k, w.batch
+        xrs, xbs, yrs, ybs = w.strides(8)
+        st = qfr.Strides(xrs, xbs, yrs, ybs)
+        W = w.make_weights()
+        copies = max(2, int(np.ceil((1 << 30) / w.stored_weight_bytes)))
+        Wd = torch.from_numpy(W.ravel()).cuda().repeat(copies).view(copies, -1)
+        wp = [Wd[c].data_ptr() for c in range(copies)]
+        xd = torch.from_numpy(w.make_x(8).ravel().copy()).cuda()
+        idd = torch.from_numpy(w.make_ids()).cuda() if w.experts else None
+        if w.fused_norm:
+            rd = torch.from_numpy(w.make_residual(8).ravel().copy()).cuda()
+            gd = torch.from_numpy(w.make_norm_weight()).cuda()
+            hd = torch.empty_like(rd)
+        for m in ms:
+            _, _, yb = qfr.row_exact_required_bytes(t, n, k, m, batch, st)
+            ys = {tag: torch.zeros(yb // 4, dtype=torch.float32, device="cuda") for tag in libs}
+
+            def run(tag, i):
+                lib, y = libs[tag], ys[tag].data_ptr()
+                if w.experts:
+                    return lib.row_exact_mv_gather(t, wp[i % copies], w.experts, idd.data_ptr(), xd.data_ptr(), y,
+                                                   n, k, m, batch, ctypes.byref(st), hs)
+                if w.fused_norm:
+                    return lib.row_exact_mv_add_rmsnorm(t, wp[i % copies], xd.data_ptr(), rd.data_ptr(),
+                                                        gd.data_ptr(), ctypes.c_float(1e-5), hd.data_ptr(), y,
+                                                        n, k, m, batch, ctypes.byref(st), hs)
+                return lib.row_exact_mv(t, wp[i % copies], xd.data_ptr(), y, n, k, m, batch, ctypes.byref(st), hs)
+
+            for tag in libs:
+                with torch.cuda.stream(stream):
+                    rc = run(tag, 0)
+                torch.cuda.synchronize()
+                if rc:
+                    raise RuntimeError(f"{name} m={m}: build {tag} returned {rc}")
+            same = torch.equal(ys["a"].view(torch.int32), ys["b"].view(torch.int32))
+            reps = int(min(200, max(30, 3e-3 / (w.weight_bytes / 2.5e12))))
+            times = {tag: [] for tag in libs}
+            for r in range(5):
+                for tag in libs:
+                    with torch.cuda.stream(stream):
+                        for i in range(3):
+                            run(tag, i)
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        torch.cuda._sleep(int(2e6))
+                        e0.record(stream)
+                        for i in range(reps):
+                            run(tag, i + r)
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                    times[tag].append(e0.elapsed_time(e1) * 1e3 / reps)
+            a, b = statistics.median(times["a"]), statistics.median(times["b"])
+            rec = {"workload": name, "m": m, "a_us": round(a, 3), "b_us": round(b, 3), "b_over_a": round(b / a, 4),
+                   "bitwise_same": bool(same),
+                   "max_abs_diff": float((ys["a"] - ys["b"]).abs().max().item()),
+                   "a_schedule": qfr.row_exact_schedule(t, n, k, m, batch).asdict()}
+            res.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+        del Wd
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        json.dump({"a": os.path.relpath(qfr._LIB_PATH, ROOT), "b": other_path, "results": res}, f, indent=1)
 
 
 if __name__ == "__main__":

@@ -108,7 +108,20 @@ def load_library() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise LibraryMissing(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
                              "(or python -m quantized_few_row_amd._build)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def load_variant(path: str) -> ctypes.CDLL:
+    """Another build of the library (e.g. one with a code-generation switch
+    overridden, ``python -m quantized_few_row_amd._build --out PATH -D ...``),
+    with the same ctypes signatures, for interleaved comparisons."""
+    if not os.path.exists(path):
+        raise LibraryMissing(f"{path} is not built")
+    return _declare(ctypes.CDLL(os.path.abspath(path)))
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     P, u32, u64 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64
     SP, SchP = ctypes.POINTER(Strides), ctypes.POINTER(Schedule)
     lib.row_exact_mv.restype = ctypes.c_int
@@ -145,7 +158,6 @@ def load_library() -> ctypes.CDLL:
     lib.row_exact_stream_read.argtypes = [P, u64, P, u32, P]
     lib.row_exact_stream_read_shapes.restype = u32
     lib.row_exact_stream_read_shapes.argtypes = []
-    _lib = lib
     return lib
 
 

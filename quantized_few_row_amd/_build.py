@@ -37,14 +37,21 @@ def compile_flags() -> list:
             "-ffp-contract=off", "-fno-fast-math", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(jobs: int = 6, verbose: bool = False) -> str:
-    """Compile every HIP source (always) and link the shared library."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 6, verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile every HIP source (always) and link the shared library.
+
+    ``out`` and ``defines`` (``NAME=VALUE`` macro overrides of the kernels'
+    code-generation switches) build a variant library elsewhere, e.g. for an
+    interleaved comparison with ``bench.py --ab``; the default is the
+    product library next to this file."""
+    objdir = BUILD if out == LIB else os.path.join(BUILD, os.path.basename(out) + ".objs")
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     cc = hipcc()
-    flags = compile_flags()
+    flags = compile_flags() + [f"-D{d}" for d in defines]
 
     def one(src: str) -> str:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
         cmd = [cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -55,14 +62,23 @@ def build(jobs: int = 6, verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr[-4000:]}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description="build the row-exact mat-vec library for gfx950")
+    ap.add_argument("-v", action="store_true", help="print the compile commands")
+    ap.add_argument("--out", default=LIB, help="library path (default: the product library in the package)")
+    ap.add_argument("-D", dest="defines", action="append", default=[], metavar="NAME=VALUE",
+                    help="override a code-generation switch (a variant build; use with --out)")
+    args = ap.parse_args()
+    if args.defines and os.path.abspath(args.out) == LIB:
+        raise SystemExit("_build: -D overrides build a variant; give it its own --out path")
+    print(build(verbose=args.v, out=os.path.abspath(args.out), defines=tuple(args.defines)))

@@ -106,3 +106,47 @@ def test_kernel_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() != h0
     (csrc / "k.hip").write_text(src.replace('"x // y"', '"x // z"'))
     assert bench.kernel_source_hash() != h0
+
+
+def test_variant_build_needs_its_own_output_path():
+    """A macro override never replaces the product library."""
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, "-m", "quantized_few_row_amd._build", "-D", "REX_HALF_STEP_LANES=0"],
+                         cwd=bench.ROOT, capture_output=True, text=True)
+    assert res.returncode != 0 and "own --out" in res.stderr
+
+
+def test_variant_objects_stay_apart_from_the_product_build(monkeypatch, tmp_path):
+    """A variant build compiles into its own object folder under the build
+    folder and links to the path it is given (compiler calls recorded, not run)."""
+    from quantized_few_row_amd import _build
+    calls = []
+
+    class Done:
+        returncode = 0
+        stderr = ""
+
+    def fake_run(cmd, **kw):
+        calls.append(cmd)
+        if "-shared" in cmd:
+            open(cmd[cmd.index("-o") + 1], "w").close()
+        return Done()
+
+    monkeypatch.setattr(_build.subprocess, "run", fake_run)
+    monkeypatch.setattr(_build, "hipcc", lambda: "hipcc")
+    monkeypatch.setattr(_build, "BUILD", str(tmp_path / "_build"))
+    out = str(tmp_path / "v" / "x.so")
+    assert _build.build(jobs=1, out=out, defines=("REX_HALF_STEP_LANES=0",)) == out
+    assert os.path.exists(out)
+    compiles = [c for c in calls if "-c" in c]
+    assert len(compiles) == len(_build.SOURCES)
+    for c in compiles:
+        assert "-DREX_HALF_STEP_LANES=0" in c
+        assert os.path.dirname(c[c.index("-o") + 1]) == str(tmp_path / "_build" / "x.so.objs")
+
+
+def test_missing_variant_is_refused():
+    import quantized_few_row_amd as qfr
+    with pytest.raises(qfr.LibraryMissing):
+        qfr.load_variant("/nonexistent/variant.so")
