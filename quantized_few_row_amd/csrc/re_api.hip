@@ -462,12 +462,28 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
                 target = (uint64_t)di.cus * 24;
             }
         }
+        // A workgroup's x stage that leaves no room for a second one on a CU
+        // (m*k*4 bytes over half the LDS): each further round of workgroups
+        // stages x again on a CU that has nothing else to run, so one round,
+        // as for more input rows, each wave walking its share of row groups,
+        // two rows per wave when every wave still gets a group (m = 2,
+        // against one row group per wave: 16384 x 11008 Q8_0 -16%, 16384 x
+        // 14336 Q6_K -20%, 14336 x 14336 Q4_K -28%, 16 x 1024 x 11008 grouped
+        // Q5_0 -18%).
+        const bool one_per_cu = di.lds_max / lds_bytes(t, m, k, kc) < 2;
+        if (one_per_cu)
+            nr = steps >= 2 && wave_rows >= 2ull * 8 * di.cus ? 2 : 1;
         s.rows_per_wave = nr;
         const uint32_t rg = nr << (6 - lpr);  // rows per group
         const uint32_t gpb = (n + rg - 1) / rg;
         const uint32_t waves = waves_per_workgroup(gpb, batch, di.cus, m, kc);
         s.waves_per_workgroup = waves;
         const uint32_t max_wgs = max_workgroups(gpb, waves, batch, di.cus);
+        if (one_per_cu) {
+            const uint32_t w1 = (uint32_t)((di.cus + batch - 1) / batch);
+            s.workgroups_per_batch = w1 < max_wgs ? w1 : max_wgs;
+            return 0;
+        }
         uint64_t w = (target / waves + batch - 1) / batch;
         // as for more input rows below: no more workgroups than keep each
         // one's weight bytes at or above the m*k*4 bytes of x it stages

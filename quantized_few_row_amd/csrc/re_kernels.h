@@ -71,6 +71,7 @@
 #ifndef REX_X_FIRST_UNC_MIN_M
 #define REX_X_FIRST_UNC_MIN_M 6
 #endif
+
 // 1: single-pass instances of types with a fixed load count per piece stage
 // x with loads that write LDS directly (see stage_x_dma).
 #ifndef REX_X_DMA
@@ -114,24 +115,11 @@ template <class V> __device__ __forceinline__ V ldv(const uint8_t *R, uint32_t o
 }
 __device__ __forceinline__ uint32_t ld16(const uint8_t *R, uint32_t off) { return *(const uint16_t *)(R + off); }
 
-// 16 bytes at an even offset o (R + o - 2 is readable when o % 4 == 2).  Reads
-// the aligned dwords around it and the last two bytes with a 16-bit load, so
-// nothing past R + o + 16 is touched.
-__device__ __forceinline__ void load16_a2(const uint8_t *R, uint32_t o, uint32_t (&out)[4]) {
-    const uint32_t sh = o & 3u;
-    const u32x4a4 r = ldv<u32x4a4>(R, o - sh);
-    const uint32_t t = ld16(R, o + 14);
-    out[0] = abyte(r.y, r.x, sh);
-    out[1] = abyte(r.z, r.y, sh);
-    out[2] = abyte(r.w, r.z, sh);
-    out[3] = abyte(t, r.w, sh);
-}
-
 // The same 16 bytes with one 2-byte-aligned dwordx4 load (the HSA runtime
 // runs the GPU in unaligned-access mode).  Measured: faster than the aligned
 // loads + realignment for Q6_K's three 16-byte fields (fewer VALU and
 // memory instructions), slower for Q8_0 and Q5_0 blocks, which keep
-// load16_a2 / the aligned loads.
+// aligned loads (realigned at multiply time).
 __device__ __forceinline__ void load16_u(const uint8_t *R, uint32_t o, uint32_t (&out)[4]) {
     const u32x4a2 r = ldv<u32x4a2>(R, o);
     out[0] = r.x; out[1] = r.y; out[2] = r.z; out[3] = r.w;
@@ -252,29 +240,37 @@ template <> struct Tr<kQ8_0> : Geo<kQ8_0> {
     static constexpr int SEG = 8;  // one scale per piece
     static constexpr int LOADS = 0;  // x staged in registers (see stage_x_dma)
     static constexpr int ITEM_DWORDS = 9;
-    struct Raw { uint32_t q[8]; uint32_t d; };
+    // Raw: the quants' bytes as loaded (eight aligned dwords around them, the
+    // last two bytes, the byte shift) and d.  They are realigned where they
+    // are multiplied: realigned at load time, the compiler waits for a
+    // piece's loads right after issuing them, before the multiply they were
+    // meant to overlap.
+    struct Raw { uint32_t w[9]; uint32_t sh; uint32_t d; };
     struct Pre { float d; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
         const uint32_t B = o0 + 34 * p;
         r.d = ld16(R, B);
         const uint32_t F = B + 2;  // quants
-        const uint32_t sh = F & 3u;
-        const u32x4a4 r0 = ldv<u32x4a4>(R, F - sh), r1 = ldv<u32x4a4>(R, F - sh + 16);
-        const uint32_t t = ld16(R, F + 30);
-        const uint32_t W9[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, t};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r.q[i] = abyte(W9[i + 1], W9[i], sh);
+        r.sh = F & 3u;
+        const u32x4a4 r0 = ldv<u32x4a4>(R, F - r.sh), r1 = ldv<u32x4a4>(R, F - r.sh + 16);
+        r.w[0] = r0.x; r.w[1] = r0.y; r.w[2] = r0.z; r.w[3] = r0.w;
+        r.w[4] = r1.x; r.w[5] = r1.y; r.w[6] = r1.z; r.w[7] = r1.w;
+        r.w[8] = ld16(R, F + 30);
         return r;
     }
+    // quant bytes 4g..4g+3
+    static __device__ __forceinline__ uint32_t qword(const Raw &r, int g) { return abyte(r.w[g + 1], r.w[g], r.sh); }
     static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d)}; }
     static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
+        const uint32_t q4 = qword(r, g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = pr.d * (float)(int8_t)(r.q[g] >> (8 * i));
+        for (int i = 0; i < 4; ++i) w[i] = pr.d * (float)(int8_t)(q4 >> (8 * i));
     }
     static __device__ __forceinline__ void deqi(const Raw &r, const Pre &, int g, float (&q)[4]) {
+        const uint32_t q4 = qword(r, g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(r.q[g] >> (8 * i));
+        for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(q4 >> (8 * i));
     }
     static __device__ __forceinline__ float scale(const Pre &pr, int) { return pr.d; }
     static __device__ __forceinline__ uint32_t vpos(uint32_t p, int g) { return 32 * p + 4 * g; }
@@ -294,34 +290,50 @@ template <> struct Tr<kQ5_0> : Geo<kQ5_0> {
     static constexpr int SEG = 8;  // one scale per piece
     static constexpr int LOADS = 0;  // x staged in registers (see stage_x_dma)
     static constexpr int ITEM_DWORDS = 6;
-    struct Raw { uint32_t qs[4]; uint32_t nqh; uint32_t d; };
-    struct Pre { float d8; };
+    // Raw: the block's bytes as loaded (the aligned dwords around its first
+    // 8 bytes, around the 16 nibble bytes plus their last two bytes, the
+    // byte shift of the block); realigned where they are multiplied (see
+    // Q8_0), into d and the inverted high bits in prep, the nibble bytes in
+    // bytes8.
+    struct Raw { uint32_t e[3]; uint32_t q[5]; uint32_t sh; };
+    struct Pre { float d8; uint32_t nqh; };
     static __device__ __forceinline__ Raw load(const uint8_t *R, uint32_t o0, uint32_t p, uint32_t) {
         Raw r;
         const uint32_t B = o0 + 22 * p;
-        const uint32_t sh = B & 3u;
-        const u32x3a4 e = ldv<u32x3a4>(R, B - sh);  // covers bytes 0..7 of the block
-        const uint32_t b0 = abyte(e.y, e.x, sh);     // d | qh.lo << 16
-        const uint32_t b1 = abyte(e.z, e.y, sh);     // qh.hi | qs[0..1] << 16
-        r.d = b0 & 0xffffu;
-        r.nqh = ~abyte(b1, b0, 2);
-        load16_a2(R, B + 6, r.qs);
+        r.sh = B & 3u;
+        const u32x3a4 e = ldv<u32x3a4>(R, B - r.sh);  // covers bytes 0..7 of the block
+        r.e[0] = e.x; r.e[1] = e.y; r.e[2] = e.z;
+        // the 16 nibble bytes at B + 6: the aligned dwords around them and
+        // their last two bytes (nothing past the block is read)
+        const uint32_t o = B + 6, shq = o & 3u;
+        const u32x4a4 q = ldv<u32x4a4>(R, o - shq);
+        r.q[0] = q.x; r.q[1] = q.y; r.q[2] = q.z; r.q[3] = q.w;
+        r.q[4] = ld16(R, o + 14);
         return r;
     }
-    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) { return {h2f(r.d) * 0.125f}; }
-    static __device__ __forceinline__ uint32_t bytes8(const Raw &r, int g) {
-        const uint32_t lo = g < 4 ? ((r.qs[g] << 3) & 0x78787878u) : ((r.qs[g & 3] >> 1) & 0x78787878u);
+    static __device__ __forceinline__ Pre prep(const Raw &r, uint32_t) {
+        const uint32_t b0 = abyte(r.e[1], r.e[0], r.sh);  // d | qh.lo << 16
+        const uint32_t b1 = abyte(r.e[2], r.e[1], r.sh);  // qh.hi | qs[0..1] << 16
+        return {h2f(b0 & 0xffffu) * 0.125f, ~abyte(b1, b0, 2)};
+    }
+    // nibble bytes 4i..4i+3 (the shift of B + 6 is that of B plus 2)
+    static __device__ __forceinline__ uint32_t qword(const Raw &r, int i) {
+        return abyte(r.q[i + 1], r.q[i], (r.sh + 2u) & 3u);
+    }
+    static __device__ __forceinline__ uint32_t bytes8(const Raw &r, const Pre &pr, int g) {
+        const uint32_t qw = qword(r, g & 3);
+        const uint32_t lo = g < 4 ? ((qw << 3) & 0x78787878u) : ((qw >> 1) & 0x78787878u);
         // bits 4g..4g+3 of ~qh -> bit 7 of bytes 0..3 (t * 0x204081 puts bit i at 8i, no carries)
-        const uint32_t t = (r.nqh >> (4 * g)) & 15u;
+        const uint32_t t = (pr.nqh >> (4 * g)) & 15u;
         return ((opaque(__umul24(t, 0x204081u)) << 7) & 0x80808080u) | lo;
     }
     static __device__ __forceinline__ void deq(const Raw &r, const Pre &pr, int g, float (&w)[4]) {
-        const uint32_t b = bytes8(r, g);
+        const uint32_t b = bytes8(r, pr, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = (float)(int8_t)(b >> (8 * i)) * pr.d8;
     }
-    static __device__ __forceinline__ void deqi(const Raw &r, const Pre &, int g, float (&q)[4]) {
-        const uint32_t b = bytes8(r, g);
+    static __device__ __forceinline__ void deqi(const Raw &r, const Pre &pr, int g, float (&q)[4]) {
+        const uint32_t b = bytes8(r, pr, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = (float)(int8_t)(b >> (8 * i));
     }

@@ -263,9 +263,18 @@ LANE_MAP_WORKLOADS: List[Workload] = [
 ]
 WORKLOADS += LANE_MAP_WORKLOADS
 HELD_OUT = ("q4_k_1024x2816", "q8_0_2816x2112")
+# Inputs whose staged x at m = 2 leaves room for one workgroup per CU, with
+# enough rows for two per wave on every wave of one round (bench.py
+# --schedule-sweep checks the chooser on them; not full-size parity cases).
+ONE_PER_CU_WORKLOADS: List[Workload] = [
+    Workload("q8_0_16384x11008", Q8_0, 16384, 11008, 1, (1, 2), 24),
+    Workload("q6_k_16384x14336", Q6_K, 16384, 14336, 1, (1, 2), 25),
+    Workload("q4_k_14336x14336", Q4_K, 14336, 14336, 1, (1, 2), 26),
+]
+ONE_PER_CU = ("q5_0_16x1024x11008_grouped",) + tuple(w.name for w in ONE_PER_CU_WORKLOADS)
 SKINNY = tuple(w.name for w in SKINNY_WORKLOADS)
 LANE_MAP = ("q6_k_4096x14336",) + tuple(w.name for w in LANE_MAP_WORKLOADS)
-BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
+BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS + ONE_PER_CU_WORKLOADS}
 
 
 def get(name: str) -> Workload:
