@@ -462,17 +462,21 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
                 target = (uint64_t)di.cus * 24;
             }
         }
-        // A workgroup's x stage that leaves no room for a second one on a CU
-        // (m*k*4 bytes over half the LDS): each further round of workgroups
-        // stages x again on a CU that has nothing else to run, so one round,
-        // as for more input rows, each wave walking its share of row groups,
-        // two rows per wave when every wave still gets a group (m = 2,
-        // against one row group per wave: 16384 x 11008 Q8_0 -16%, 16384 x
+        // A workgroup's x stage that leaves room for at most one more on a
+        // CU (m*k*4 bytes over a third of the LDS): each further round of
+        // workgroups stages x again on a CU with little else to run, so one
+        // workgroup per CU, each wave walking its share of row groups; at
+        // m = 2 two rows per wave when waves then get more than one group
+        // (4096 x 8192 Q8_0, one group of two rows per wave: 12% slower than
+        // two single rows).
+        // Against the rule above, m = 2: 16384 x 11008 Q8_0 -16%, 16384 x
         // 14336 Q6_K -20%, 14336 x 14336 Q4_K -28%, 16 x 1024 x 11008 grouped
-        // Q5_0 -18%).
-        const bool one_per_cu = di.lds_max / lds_bytes(t, m, k, kc) < 2;
+        // Q5_0 -18%, 4096 x 8192 Q8_0 -9%, 14336 x 8192 Q4_K -17%; m = 1:
+        // 14336 x 14336 Q4_K -9%, 16384 x 14336 Q6_K -3% (within 2% of it
+        // on 4096 x 14336 Q8_0, 8192 x 14336 Q6_K, 16384 x 8192 Q6_K at m = 2).
+        const bool one_per_cu = di.lds_max / lds_bytes(t, m, k, kc) < 3;
         if (one_per_cu)
-            nr = steps >= 2 && wave_rows >= 2ull * 8 * di.cus ? 2 : 1;
+            nr = m == 2 && steps >= 2 && wave_rows > 2ull * 8 * di.cus ? 2 : 1;
         s.rows_per_wave = nr;
         const uint32_t rg = nr << (6 - lpr);  // rows per group
         const uint32_t gpb = (n + rg - 1) / rg;

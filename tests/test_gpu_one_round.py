@@ -1,12 +1,12 @@
-"""Inputs whose staged x fills more than half of a CU's LDS.
+"""Inputs whose staged x fills more than a third of a CU's LDS.
 
-With m*k*4 bytes of x (plus pads) over 80 KB, one workgroup's stage leaves
-no room for a second on a CU, and the default schedule launches one round of
-workgroups (at most one per CU), two rows per wave where every wave still
-gets a row group.  Packing is inert: its bits must equal a pinned schedule
-of one row group per wave (several rounds of workgroups), and its outputs
-stay within the float64 oracle's tolerance (row ranges at the start, middle
-and end of every batch entry).
+With m*k*4 bytes of x (plus pads) over about 53 KB, one workgroup's stage
+leaves room for at most one more on a CU, and the default schedule launches
+one workgroup per CU, two rows per wave at m = 2 where every wave still gets
+a row group.  Packing is inert: its bits must equal a pinned schedule of one
+row group per wave (several rounds of workgroups), and its outputs stay
+within the float64 oracle's tolerance (row ranges at the start, middle and
+end of every batch entry).
 """
 import numpy as np
 import pytest
@@ -21,12 +21,15 @@ pytestmark = pytest.mark.gpu
 
 # (type, n, k, batch, m): x stages of 92 KB (Q8_0 k = 10240 at m = 2 and
 # k = 20480 at m = 1, 64-lane rows), 99 KB (Q5_0 k = 11008 at m = 2, 32-lane
-# rows) and 122 KB (Q6_K k = 14336 at m = 2, piece-major, 32-lane rows)
+# rows), 122 KB (Q6_K k = 14336 at m = 2, piece-major, 32-lane rows), 72 KB
+# (Q8_0 k = 8192 at m = 2) and 57 KB (Q4_K k = 14336 at m = 1, 32-lane rows)
 SHAPES = [
     (wl.Q8_0, 4096, 10240, 1, 2),
     (wl.Q8_0, 4096, 20480, 1, 1),
     (wl.Q5_0, 1024, 11008, 8, 2),
     (wl.Q6_K, 4096, 14336, 2, 2),
+    (wl.Q8_0, 4096, 8192, 1, 2),
+    (wl.Q4_K, 4096, 14336, 2, 1),
 ]
 IDS = [f"{wl.TYPE_NAMES[t]}_{b}x{n}x{k}_m{m}" for t, n, k, b, m in SHAPES]
 

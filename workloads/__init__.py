@@ -263,13 +263,16 @@ LANE_MAP_WORKLOADS: List[Workload] = [
 ]
 WORKLOADS += LANE_MAP_WORKLOADS
 HELD_OUT = ("q4_k_1024x2816", "q8_0_2816x2112")
-# Inputs whose staged x at m = 2 leaves room for one workgroup per CU, with
-# enough rows for two per wave on every wave of one round (bench.py
-# --schedule-sweep checks the chooser on them; not full-size parity cases).
+# Inputs whose staged x at m = 1 or 2 leaves room for one or two workgroups
+# per CU, with enough rows for two per wave on every wave of one workgroup per
+# CU (bench.py --schedule-sweep checks the chooser on them; not full-size
+# parity cases).
 ONE_PER_CU_WORKLOADS: List[Workload] = [
     Workload("q8_0_16384x11008", Q8_0, 16384, 11008, 1, (1, 2), 24),
     Workload("q6_k_16384x14336", Q6_K, 16384, 14336, 1, (1, 2), 25),
     Workload("q4_k_14336x14336", Q4_K, 14336, 14336, 1, (1, 2), 26),
+    Workload("q8_0_4096x8192", Q8_0, 4096, 8192, 1, (1, 2), 27),
+    Workload("q4_k_14336x8192", Q4_K, 14336, 8192, 1, (1, 2), 28),
 ]
 ONE_PER_CU = ("q5_0_16x1024x11008_grouped",) + tuple(w.name for w in ONE_PER_CU_WORKLOADS)
 SKINNY = tuple(w.name for w in SKINNY_WORKLOADS)
