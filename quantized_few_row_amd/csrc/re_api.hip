@@ -439,21 +439,22 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
     if (m <= 2 && kc >= k) {
         // Few input rows: the weight loads dominate.  Measured best on
         // MI355X: about 32 waves per CU over the whole grid (the hardware
-        // balances the tail across workgroups), one row group per wave while
-        // the rows allow it, single rows beyond that.  A row group of a
-        // single wave step is one item, and a wave with one item has nothing
-        // to multiply while its loads are in flight: rows of one step take
+        // balances the tail across workgroups), single rows.  Where the
+        // rows would give each of those waves between one and two of them,
         // single rows on 24 waves per CU instead, so each wave walks two or
-        // more of them (Q4_K 14336 x 4096: 12.3 -> 10.8 us at m = 1).
+        // more: a row of one wave step is one item, and a wave with one item
+        // has nothing to multiply while its loads are in flight (Q4_K
+        // 14336 x 4096: 12.3 -> 10.8 us at m = 1); for rows of several
+        // steps, against two rows per wave on 32 waves per CU (one row group
+        // per wave): 14336 x 8192 Q4_K -11%, 14336 x 4096 Q8_0 -7%, 14336 x
+        // 8192 Q6_K -24% at m = 1, 14336 x 4096 Q8_0 -4% at m = 2.
         uint64_t target = (uint64_t)di.cus * 32;
         const uint32_t lpr = lane_map_log2(t, k, 1);
         const uint64_t wave_rows = rows >> (6 - lpr);  // rows / slots per wave
         const uint32_t steps = (pieces_of(t, k) + (1u << lpr) - 1) >> lpr;
         uint32_t nr = 1;
         if (wave_rows > target && wave_rows <= 2 * target) {
-            if (steps >= 2) {
-                nr = 2;
-            } else if (m == 2) {
+            if (m == 2 && steps < 2) {
                 // two input rows: 2 rows per wave on 8 waves per CU, each
                 // wave walking several groups (Q4_K 14336 x 4096: -8%)
                 nr = 2;

@@ -263,21 +263,24 @@ LANE_MAP_WORKLOADS: List[Workload] = [
 ]
 WORKLOADS += LANE_MAP_WORKLOADS
 HELD_OUT = ("q4_k_1024x2816", "q8_0_2816x2112")
-# Inputs whose staged x at m = 1 or 2 leaves room for one or two workgroups
-# per CU, with enough rows for two per wave on every wave of one workgroup per
-# CU (bench.py --schedule-sweep checks the chooser on them; not full-size
-# parity cases).
-ONE_PER_CU_WORKLOADS: List[Workload] = [
+# Large inputs at m = 1 and 2 for the chooser's rules on few input rows
+# (bench.py --schedule-sweep checks it on them; not full-size parity cases):
+# staged x leaving room for one or two workgroups per CU, with enough rows for
+# two per wave on every wave of one workgroup per CU; and rows that would give
+# each of 32 waves per CU between one and two rows.
+LARGE_WORKLOADS: List[Workload] = [
     Workload("q8_0_16384x11008", Q8_0, 16384, 11008, 1, (1, 2), 24),
     Workload("q6_k_16384x14336", Q6_K, 16384, 14336, 1, (1, 2), 25),
     Workload("q4_k_14336x14336", Q4_K, 14336, 14336, 1, (1, 2), 26),
     Workload("q8_0_4096x8192", Q8_0, 4096, 8192, 1, (1, 2), 27),
     Workload("q4_k_14336x8192", Q4_K, 14336, 8192, 1, (1, 2), 28),
+    Workload("q8_0_14336x4096", Q8_0, 14336, 4096, 1, (1, 2), 29),
+    Workload("q6_k_14336x8192", Q6_K, 14336, 8192, 1, (1, 2), 30),
 ]
-ONE_PER_CU = ("q5_0_16x1024x11008_grouped",) + tuple(w.name for w in ONE_PER_CU_WORKLOADS)
+LARGE = ("q5_0_16x1024x11008_grouped",) + tuple(w.name for w in LARGE_WORKLOADS)
 SKINNY = tuple(w.name for w in SKINNY_WORKLOADS)
 LANE_MAP = ("q6_k_4096x14336",) + tuple(w.name for w in LANE_MAP_WORKLOADS)
-BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS + ONE_PER_CU_WORKLOADS}
+BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS + LARGE_WORKLOADS}
 
 
 def get(name: str) -> Workload:
