@@ -453,7 +453,12 @@ int default_schedule(int t, uint32_t n, uint32_t k, uint32_t m, uint32_t batch, 
         const uint64_t wave_rows = rows >> (6 - lpr);  // rows / slots per wave
         const uint32_t steps = (pieces_of(t, k) + (1u << lpr) - 1) >> lpr;
         uint32_t nr = 1;
-        if (wave_rows > target && wave_rows <= 2 * target) {
+        if (m == 2 && steps >= 2) {
+            // two input rows, rows of several wave steps: 16 waves per CU
+            // (against 24 or 32: 14336 x 6144 Q4_K -16%, 14336 x 4096 Q8_0
+            // -7%, 12288 x 4096 Q8_0 and BF16 -2%, 14336 x 2048 F16 +0.4%)
+            target = (uint64_t)di.cus * 16;
+        } else if (wave_rows > target && wave_rows <= 2 * target) {
             if (m == 2 && steps < 2) {
                 // two input rows: 2 rows per wave on 8 waves per CU, each
                 // wave walking several groups (Q4_K 14336 x 4096: -8%)

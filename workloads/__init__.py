@@ -276,6 +276,7 @@ LARGE_WORKLOADS: List[Workload] = [
     Workload("q4_k_14336x8192", Q4_K, 14336, 8192, 1, (1, 2), 28),
     Workload("q8_0_14336x4096", Q8_0, 14336, 4096, 1, (1, 2), 29),
     Workload("q6_k_14336x8192", Q6_K, 14336, 8192, 1, (1, 2), 30),
+    Workload("q4_k_14336x6144", Q4_K, 14336, 6144, 1, (1, 2), 31),
 ]
 LARGE = ("q5_0_16x1024x11008_grouped",) + tuple(w.name for w in LARGE_WORKLOADS)
 SKINNY = tuple(w.name for w in SKINNY_WORKLOADS)
