@@ -950,7 +950,11 @@ __device__ __forceinline__ void norm_partials(double *part, float *__restrict__ 
                                               const float *__restrict__ xb, const float *__restrict__ rb,
                                               const float *__restrict__ g, float *__restrict__ hb, uint32_t xrs,
                                               uint32_t k, uint32_t wave, uint32_t nwaves, uint32_t lane) {
-    constexpr int JB = M >= 4 ? 2 : 1;  // rows per batch
+    // rows per batch: from m = 4, half the rows (with 256-thread row
+    // groups, a thread's rows of one parity in one batch: one round trip
+    // for x and r instead of two; fused Q8_0 4096 x 4096 at m = 5..8: -2
+    // to -6% against two rows per batch)
+    constexpr int JB = M >= 4 ? (M + 1) / 2 : 1;
     constexpr int CB = M <= 2 ? 2 : 4;  // chunks per row per batch (few rows: registers for occupancy)
     const uint32_t n4 = k >> 2;
     const uint32_t nt = nwaves << 6, tid = (wave << 6) + lane;
