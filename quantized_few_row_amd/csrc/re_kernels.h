@@ -955,7 +955,9 @@ __device__ __forceinline__ void norm_partials(double *part, float *__restrict__ 
     // for x and r instead of two; fused Q8_0 4096 x 4096 at m = 5..8: -2
     // to -6% against two rows per batch)
     constexpr int JB = M >= 4 ? (M + 1) / 2 : 1;
-    constexpr int CB = M <= 2 ? 2 : 4;  // chunks per row per batch (few rows: registers for occupancy)
+    // chunks per row per batch (few rows: registers for occupancy; 4 at m <= 2
+    // measured 3% slower on fused Q8_0 4096 x 4096)
+    constexpr int CB = M <= 2 ? 2 : 4;
     const uint32_t n4 = k >> 2;
     const uint32_t nt = nwaves << 6, tid = (wave << 6) + lane;
     const bool wide = (nt & 255u) == 0;
