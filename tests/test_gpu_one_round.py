@@ -31,16 +31,26 @@ SHAPES = [
     (wl.Q8_0, 4096, 8192, 1, 2),
     (wl.Q4_K, 4096, 14336, 2, 1),
 ]
-IDS = [f"{wl.TYPE_NAMES[t]}_{b}x{n}x{k}_m{m}" for t, n, k, b, m in SHAPES]
+# The other rules for few input rows on large inputs (x of 16-24 KB, several
+# workgroups per CU): rows that give each of 32 waves per CU between one and
+# two of them (single rows on 24 waves per CU; Q8_0 14336 x 4096 at m = 1),
+# and rows of several wave steps at m = 2 (16 waves per CU; Q4_K 14336 x 6144,
+# 32-lane rows).  Only the bits and the tolerance are checked for these.
+OTHER = [
+    (wl.Q8_0, 14336, 4096, 1, 1),
+    (wl.Q4_K, 14336, 6144, 1, 2),
+]
+IDS = [f"{wl.TYPE_NAMES[t]}_{b}x{n}x{k}_m{m}" for t, n, k, b, m in SHAPES + OTHER]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=IDS)
+@pytest.mark.parametrize("shape", SHAPES + OTHER, ids=IDS)
 def test_one_round_default_is_inert_and_within_tolerance(shape):
     t, n, k, batch, m = shape
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     d = row_exact_schedule(t, n, k, m, batch)
     assert d.k_split == 1 and d.k_chunk >= k
-    assert d.workgroups_per_batch * batch <= cus + batch - 1, d.asdict()
+    if shape in SHAPES:
+        assert d.workgroups_per_batch * batch <= cus + batch - 1, d.asdict()
     W = wl.weights(t, n * batch, k, seed=3100 + 100 * t + m)
     x = wl.activations(batch * m, k, seed=3200 + 100 * t + m)
     Wd, xd = to_dev(W.ravel()), to_dev(x.ravel())
