@@ -1378,11 +1378,12 @@ __global__ void __launch_bounds__(512) mv_kernel(const MvArgs a) {
             if (DEPTH == 2) fetch_item<T, NR, SUB, UP>(Wb, a, lg, ls, g1, nwaves, S, li, slot, B);
         };
         if constexpr (NORM) {
-            // as below for the plain product: from REX_LATE_HALF_MIN_M input
-            // rows on, the upper half of the waves request their first items
-            // after the normalisation prologue (fused Q8_0 4096 x 4096 at
-            // m = 5..8: -2% to -4%)
-            const bool late = M >= REX_LATE_HALF_MIN_M && nwaves >= 2 && wave >= (nwaves >> 1);
+            // at every m, the upper half of the waves request their first
+            // items after the normalisation prologue (as the plain product
+            // does from REX_LATE_HALF_MIN_M input rows on): the prologue's x
+            // and r loads then wait behind half of the weights (fused Q8_0
+            // 4096 x 4096: m = 1..4 -4 to -8%, m = 5..8 -2 to -4%)
+            const bool late = nwaves >= 2 && wave >= (nwaves >> 1);
             if (!late) prefetch_first();
             norm_partials<T, M, true>(part, xs, XS, xb, a.r + b * a.xbs, a.g,
                                       (a.h && w == 0) ? a.h + b * a.xbs : nullptr, a.xrs, a.k, wave, nwaves, lane);
