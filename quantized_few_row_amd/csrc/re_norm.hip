@@ -31,13 +31,15 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(const NormArgs a) {
     const uint32_t n4 = a.k >> 2;
     double ss = 0.0;
     for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
-        f32x4 xv[kChunksAhead], rv[kChunksAhead];
+        // x, r and g requested together: one memory round trip per batch
+        f32x4 xv[kChunksAhead], rv[kChunksAhead], gv[kChunksAhead];
 #pragma unroll
         for (int c = 0; c < kChunksAhead; ++c) {
             const uint32_t q = q0 + 256u * c;
             if (q < n4) {
                 xv[c] = *(const f32x4 *)(xr + 4 * q);
                 rv[c] = *(const f32x4 *)(rr + 4 * q);
+                if (a.g) gv[c] = *(const f32x4 *)(a.g + 4 * q);
             }
         }
 #pragma unroll
@@ -49,7 +51,12 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(const NormArgs a) {
                 for (int e = 0; e < 4; ++e) h[e] = xv[c][e] + rv[c][e];
                 if (hr) *(f32x4 *)(hr + 4 * q) = h;
                 ss = fold4(ss, h);
-                *(f32x4 *)(ur + 4 * q) = times_g(h, a.g, 4 * q);
+                f32x4 u = h;
+                if (a.g) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) u[e] = h[e] * gv[c][e];
+                }
+                *(f32x4 *)(ur + 4 * q) = u;
             }
         }
     }
@@ -108,34 +115,42 @@ __global__ void __launch_bounds__(256) residual_rows_kernel(const ResidualArgs a
     const double inv1 = block_inv_rms(s1, part, lane, wave, a.k, a.eps);
     double s2 = 0.0;
     for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
-        f32x4 xv[kChunksAhead], hv[kChunksAhead];
+        // x, h and the weights w, c, w2 requested together: one memory
+        // round trip per batch
+        f32x4 xv[kChunksAhead], hv[kChunksAhead], wv[kChunksAhead], cv[kChunksAhead], w2v[kChunksAhead];
 #pragma unroll
         for (int c = 0; c < kChunksAhead; ++c) {
             const uint32_t q = q0 + 256u * c;
             if (q < n4) {
                 xv[c] = *(const f32x4 *)(xr + 4 * q);
                 hv[c] = *(const f32x4 *)(hr + 4 * q);
+                wv[c] = a.w ? *(const f32x4 *)(a.w + 4 * q) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+                if (a.c) cv[c] = *(const f32x4 *)(a.c + 4 * q);
+                if (a.w2) w2v[c] = *(const f32x4 *)(a.w2 + 4 * q);
             }
         }
 #pragma unroll
         for (int c = 0; c < kChunksAhead; ++c) {
             const uint32_t q = q0 + 256u * c;
             if (q < n4) {
-                const f32x4 wv = a.w ? *(const f32x4 *)(a.w + 4 * q) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
                 f32x4 hs;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float t = (float)((double)xv[c][e] * inv1 * (double)wv[e]);
+                    const float t = (float)((double)xv[c][e] * inv1 * (double)wv[c][e]);
                     hs[e] = hv[c][e] + t;
                 }
                 if (a.c) {
-                    const f32x4 cv = *(const f32x4 *)(a.c + 4 * q);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) hs[e] = hs[e] * cv[e];
+                    for (int e = 0; e < 4; ++e) hs[e] = hs[e] * cv[c][e];
                 }
                 if (ho) *(f32x4 *)(ho + 4 * q) = hs;
                 s2 = fold4(s2, hs);
-                *(f32x4 *)(ur + 4 * q) = times_g(hs, a.w2, 4 * q);
+                f32x4 u = hs;
+                if (a.w2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) u[e] = hs[e] * w2v[c][e];
+                }
+                *(f32x4 *)(ur + 4 * q) = u;
             }
         }
     }
