@@ -100,14 +100,34 @@ __global__ void __launch_bounds__(256) residual_rows_kernel(const ResidualArgs a
     float *__restrict__ ur = a.u + ((uint64_t)b * a.m + j) * a.k;
     const uint32_t n4 = a.k >> 2;
     __shared__ double part[4];
-    double s1 = 0.0;
-    for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
-        f32x4 xv[kChunksAhead];
+    // With one batch per thread (k <= 4096) every input is requested once,
+    // up front, and the second pass works from registers; otherwise each
+    // pass requests its batch's inputs together.
+    const bool one_batch = n4 <= 256u * kChunksAhead;
+    f32x4 xv[kChunksAhead], hv[kChunksAhead], wv[kChunksAhead], cv[kChunksAhead], w2v[kChunksAhead];
+    auto load_rest = [&](uint32_t q0) {
+#pragma unroll
+        for (int c = 0; c < kChunksAhead; ++c) {
+            const uint32_t q = q0 + 256u * c;
+            if (q < n4) {
+                hv[c] = *(const f32x4 *)(hr + 4 * q);
+                wv[c] = a.w ? *(const f32x4 *)(a.w + 4 * q) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+                if (a.c) cv[c] = *(const f32x4 *)(a.c + 4 * q);
+                if (a.w2) w2v[c] = *(const f32x4 *)(a.w2 + 4 * q);
+            }
+        }
+    };
+    auto load_x = [&](uint32_t q0) {
 #pragma unroll
         for (int c = 0; c < kChunksAhead; ++c) {
             const uint32_t q = q0 + 256u * c;
             if (q < n4) xv[c] = *(const f32x4 *)(xr + 4 * q);
         }
+    };
+    double s1 = 0.0;
+    for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
+        load_x(q0);
+        if (one_batch) load_rest(q0);
 #pragma unroll
         for (int c = 0; c < kChunksAhead; ++c)
             if (q0 + 256u * c < n4) s1 = fold4(s1, xv[c]);
@@ -115,19 +135,9 @@ __global__ void __launch_bounds__(256) residual_rows_kernel(const ResidualArgs a
     const double inv1 = block_inv_rms(s1, part, lane, wave, a.k, a.eps);
     double s2 = 0.0;
     for (uint32_t q0 = v; q0 < n4; q0 += 256u * kChunksAhead) {
-        // x, h and the weights w, c, w2 requested together: one memory
-        // round trip per batch
-        f32x4 xv[kChunksAhead], hv[kChunksAhead], wv[kChunksAhead], cv[kChunksAhead], w2v[kChunksAhead];
-#pragma unroll
-        for (int c = 0; c < kChunksAhead; ++c) {
-            const uint32_t q = q0 + 256u * c;
-            if (q < n4) {
-                xv[c] = *(const f32x4 *)(xr + 4 * q);
-                hv[c] = *(const f32x4 *)(hr + 4 * q);
-                wv[c] = a.w ? *(const f32x4 *)(a.w + 4 * q) : f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-                if (a.c) cv[c] = *(const f32x4 *)(a.c + 4 * q);
-                if (a.w2) w2v[c] = *(const f32x4 *)(a.w2 + 4 * q);
-            }
+        if (!one_batch) {
+            load_x(q0);
+            load_rest(q0);
         }
 #pragma unroll
         for (int c = 0; c < kChunksAhead; ++c) {
